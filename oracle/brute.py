@@ -1,0 +1,136 @@
+"""Scalar-loop oracle of the Spatial-Transformer block, for tiny shapes.
+
+TEST INFRASTRUCTURE ONLY.  Written independently of ``oracle.block``: Python
+floats (IEEE double), nested lists and explicit loops, stdlib ``math`` only.
+It exists to cross-check the vectorised oracle element by element.  Same
+definition and readings as ``oracle.block`` (pages cited there): GroupNorm(32
+contiguous channel groups, eps 1e-6, population variance) -> tokens n = i*W+j
+-> proj_in -> depth x [LN -> self-attn -> +, LN -> cross-attn over the
+un-normalised context -> +, LN -> GEGLU(value = first half, gate = second
+half, exact-erf GELU) -> Linear -> +] -> proj_out -> NCHW -> + x.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _mean(vals):
+    s = 0.0
+    for v in vals:
+        s += v
+    return s / len(vals)
+
+
+def _lin(vec, w, b):
+    """One output row: out[o] = sum_i vec[i] * w[o][i] + b[o]."""
+    out = []
+    for o in range(len(w)):
+        acc = 0.0
+        row = w[o]
+        for i in range(len(vec)):
+            acc += vec[i] * row[i]
+        out.append(acc + (b[o] if b is not None else 0.0))
+    return out
+
+
+def _ln(vec, g, bt, eps=1e-5):
+    m = _mean(vec)
+    var = _mean([(v - m) * (v - m) for v in vec])
+    r = 1.0 / math.sqrt(var + eps)
+    return [(vec[c] - m) * r * g[c] + bt[c] for c in range(len(vec))]
+
+
+def _attend(qrow, keys, vals, heads):
+    """Attention of one query row against lists of key/value rows."""
+    C = len(qrow)
+    d = C // heads
+    out = [0.0] * C
+    for hd in range(heads):
+        lo = hd * d
+        scores = []
+        for kr in keys:
+            s = 0.0
+            for j in range(d):
+                s += qrow[lo + j] * kr[lo + j]
+            scores.append(s / math.sqrt(d))
+        mx = max(scores)
+        ex = [math.exp(s - mx) for s in scores]
+        tot = sum(ex)
+        for j in range(d):
+            acc = 0.0
+            for n in range(len(keys)):
+                acc += ex[n] / tot * vals[n][lo + j]
+            out[lo + j] = acc
+    return out
+
+
+def _gelu(g):
+    return 0.5 * g * (1.0 + math.erf(g / math.sqrt(2.0)))
+
+
+def _tolist(a):
+    return a.tolist() if hasattr(a, "tolist") else a
+
+
+def block_forward(x, ctx, params, heads, groups=32, gn_eps=1e-6):
+    """Return y as nested lists [B][C][H][W]."""
+    x = _tolist(x)
+    ctx = _tolist(ctx)
+    P = {k: _tolist(v) for k, v in params.items() if k != "layers"}
+    layers = [{k: _tolist(v) for k, v in lw.items()} for lw in params["layers"]]
+    B, C, H, W = len(x), len(x[0]), len(x[0][0]), len(x[0][0][0])
+    cg = C // groups
+    y = []
+    for b in range(B):
+        # GroupNorm
+        z = [[[0.0] * W for _ in range(H)] for _ in range(C)]
+        for g in range(groups):
+            vals = [x[b][c][i][j] for c in range(g * cg, (g + 1) * cg)
+                    for i in range(H) for j in range(W)]
+            m = _mean(vals)
+            var = _mean([(v - m) * (v - m) for v in vals])
+            r = 1.0 / math.sqrt(var + gn_eps)
+            for c in range(g * cg, (g + 1) * cg):
+                for i in range(H):
+                    for j in range(W):
+                        z[c][i][j] = (x[b][c][i][j] - m) * r * P["gn_w"][c] + P["gn_b"][c]
+        # tokens in row-major pixel order, then proj_in
+        tok = []
+        for i in range(H):
+            for j in range(W):
+                tok.append(_lin([z[c][i][j] for c in range(C)],
+                                P["proj_in_w"], P.get("proj_in_b")))
+        ctx_b = ctx[b]
+        for lw in layers:
+            u = [_ln(t, lw["ln1_w"], lw["ln1_b"]) for t in tok]
+            qs = [_lin(r, lw["q1_w"], lw.get("q1_b")) for r in u]
+            ks = [_lin(r, lw["k1_w"], lw.get("k1_b")) for r in u]
+            vs = [_lin(r, lw["v1_w"], lw.get("v1_b")) for r in u]
+            new = []
+            for n in range(len(tok)):
+                o = _lin(_attend(qs[n], ks, vs, heads), lw["o1_w"], lw.get("o1_b"))
+                new.append([tok[n][c] + o[c] for c in range(C)])
+            tok = new
+            u = [_ln(t, lw["ln2_w"], lw["ln2_b"]) for t in tok]
+            qs = [_lin(r, lw["q2_w"], lw.get("q2_b")) for r in u]
+            ks = [_lin(r, lw["k2_w"], lw.get("k2_b")) for r in ctx_b]
+            vs = [_lin(r, lw["v2_w"], lw.get("v2_b")) for r in ctx_b]
+            new = []
+            for n in range(len(tok)):
+                o = _lin(_attend(qs[n], ks, vs, heads), lw["o2_w"], lw.get("o2_b"))
+                new.append([tok[n][c] + o[c] for c in range(C)])
+            tok = new
+            new = []
+            for t in tok:
+                u = _ln(t, lw["ln3_w"], lw["ln3_b"])
+                zz = _lin(u, lw["ff1_w"], lw.get("ff1_b"))
+                F = len(zz) // 2
+                f = [zz[k] * _gelu(zz[F + k]) for k in range(F)]
+                o = _lin(f, lw["ff2_w"], lw.get("ff2_b"))
+                new.append([t[c] + o[c] for c in range(C)])
+            tok = new
+        out = [_lin(t, P["proj_out_w"], P.get("proj_out_b")) for t in tok]
+        yb = [[[out[i * W + j][c] + x[b][c][i][j] for j in range(W)]
+               for i in range(H)] for c in range(C)]
+        y.append(yb)
+    return y
