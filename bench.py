@@ -1,0 +1,159 @@
+"""Benchmark of the Spatial-Transformer block on one MI355X.
+
+One step = one st_block_forward of the whole block (GroupNorm, proj_in, every
+layer's self-attention, cross-attention and GEGLU feed-forward, proj_out) on
+the SDXL Down1 workload: B=2, C=640, 64x64 latent (4096 tokens per sample),
+10 heads of 64, context [2, 77, 2048], depth 2, bf16 storage, seeded
+random-init weights (N(0, 0.02^2)) and N(0, 1) inputs already resident in HBM.
+
+Prints one JSON line: block tokens/s as `value`, the self-attention kernel's
+achieved TFLOP/s against the bf16 MFMA peak as `roofline` (its duration from
+HIP events recorded by the library around each self-attention launch, on the
+stream it runs on, during the timed region), and the fp64 CPU oracle timed on
+the host as `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "spatial-transformer block tokens/s + attention TFLOP/s (% bf16 MFMA peak)"
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+DEFAULT_WORKLOAD = 3       # index into synth.CONFIGS: SDXL Down1, 64x64, depth 2
+
+
+def attention_flops(cfg) -> float:
+    """QK^T and PV of one self-attention launch: 4 * B * heads * N^2 * 64."""
+    return 4.0 * cfg.B * cfg.heads * float(cfg.N) ** 2 * 64
+
+
+def block_flops(cfg) -> float:
+    """All GEMM and attention FLOPs of one forward (2 per multiply-add)."""
+    T, C, D, depth, B, N = cfg.T, cfg.C, cfg.D_ctx, cfg.depth, cfg.B, cfg.N
+    per_layer = 36.0 * T * C * C + attention_flops(cfg) + 4.0 * B * N * 77 * C \
+        + 4.0 * B * 77 * D * C
+    return 4.0 * T * C * C + depth * per_layer
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle as it stands: one full forward of the same workload."""
+    import oracle.block as ob
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.T / dt, "unit": "tokens/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"one full fp64 forward of the same workload ({cfg.T} tokens), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=DEFAULT_WORKLOAD,
+                    help="workload index (default: the SDXL Down1 block)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true",
+                    help="also time every kernel kind in an extra untimed pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the block is not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from latent_diffusion_net_amd import (STBlock, array_to_device,
+                                          params_to_device, synth)
+
+    cfg = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(cfg, synth.config_seed(args.config))
+    dev = "cuda:0"
+    p = params_to_device(inp["params"], cfg.dtype, dev)
+    x = array_to_device(inp["x"], cfg.dtype, dev)
+    ctx = array_to_device(inp["ctx"], cfg.dtype, dev)
+    y = torch.empty_like(x)
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth,
+                  cfg.dtype, p)
+    del p
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        blk.forward(x, ctx, y, stream)
+    torch.cuda.synchronize()
+    blk.read_timing()
+    blk.set_timing(["self_attn"])
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.forward(x, ctx, y, stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    timing = blk.read_timing()
+    blk.set_timing([])
+
+    ms_per_step = dt * 1e3 / args.steps
+    tokens_per_s = cfg.T / (dt / args.steps)
+    attn = timing.get("self_attn", {"ms": float("nan"), "launches": 1})
+    attn_s = attn["ms"] / 1e3 / attn["launches"]
+    attn_tflops = attention_flops(cfg) / attn_s / 1e12
+
+    kernels = None
+    if args.kernels:
+        from latent_diffusion_net_amd.binding import KERNEL_KINDS
+        blk.set_timing(KERNEL_KINDS)
+        for _ in range(5):
+            blk.forward(x, ctx, y, stream)
+        torch.cuda.synchronize()
+        kt = blk.read_timing()
+        blk.set_timing([])
+        kernels = {k: round(v["ms"] / 5 * 1e3, 2) for k, v in kt.items()}
+    blk.close()
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded random-init weights N(0,0.02^2), x and ctx N(0,1))",
+        "config": {"workload": cfg.name, "B": cfg.B, "C": cfg.C, "H": cfg.H,
+                   "W": cfg.W, "heads": cfg.heads, "D_ctx": cfg.D_ctx,
+                   "depth": cfg.depth, "tokens_per_step": cfg.T},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_bf16_kernel (self-attention)",
+                     "us_per_launch": attn_s * 1e6,
+                     "flops_per_launch": attention_flops(cfg)},
+        "block_tflops": block_flops(cfg) / (dt / args.steps) / 1e12,
+    }
+    if kernels is not None:
+        result["kernel_us_per_step"] = kernels
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

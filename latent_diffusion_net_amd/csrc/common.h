@@ -1,0 +1,92 @@
+// Shared device-side definitions of the Spatial-Transformer block kernels
+// (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stb {
+
+typedef uint16_t bf16_t;   // bfloat16 storage (upper half of an fp32)
+typedef _Float16 f16_t;    // IEEE half storage
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHeadDim = 64;
+constexpr int kCtxLen = 77;
+constexpr int kGroups = 32;
+
+__device__ __forceinline__ float bf2f(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float v) {
+  __bf16 b = static_cast<__bf16>(v);
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  bf16x2 r;
+  r[0] = static_cast<__bf16>(lo);
+  r[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  f16x2 r;
+  r[0] = static_cast<_Float16>(lo);
+  r[1] = static_cast<_Float16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two 16-bit values of type T packed in one dword, rounded to nearest even.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) { return pack2bf(lo, hi); }
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) { return pack2h(lo, hi); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f32<f16_t>(f16_t v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v) { return static_cast<f16_t>(v); }
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// GELU in its exact form: g * Phi(g) = g/2 * (1 + erf(g / sqrt 2)).
+__device__ __forceinline__ float gelu_erf(float g) {
+  return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+}
+
+// 32x32x16 MFMA with fp32 accumulation, bf16 or fp16 operands (8 per lane).
+__device__ __forceinline__ floatx16 mfma32x32x16(const uint4& a, const uint4& b,
+                                                 floatx16 c, bf16_t) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32x32x16(const uint4& a, const uint4& b,
+                                                 floatx16 c, f16_t) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+}  // namespace stb

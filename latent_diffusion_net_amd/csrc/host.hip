@@ -1,0 +1,671 @@
+// C ABI of the Spatial-Transformer block: argument validation, weight
+// repacking into library-owned device memory, workspace planning and the
+// launch schedule of one forward.  Declared in include/st_block.h.
+//
+// Launch schedule of one forward (bf16 storage):
+//   GroupNorm statistics            x                     -> (mean, rstd)[B*32]
+//   GroupNorm apply + to tokens     x                     -> u [T][C] bf16
+//   proj_in GEMM                    u, W_in               -> h [T][C] fp32
+//   context K/V GEMM (all layers)   ctx, [Wk2;Wv2]*depth  -> Kc, Vc^T per layer
+//   per layer:
+//     LayerNorm 1                   h                     -> u
+//     Q/K/V GEMM                    u, [Wq1;Wk1;Wv1]      -> Q, K, V^T (per head)
+//     self-attention                Q, K, V^T             -> O [T][C] bf16
+//     out-projection GEMM           O, Wo1                -> h += .
+//     LayerNorm 2, cross Q GEMM     h, Wq2                -> Q
+//     cross-attention               Q, Kc, Vc^T           -> O
+//     out-projection GEMM           O, Wo2                -> h += .
+//     LayerNorm 3, FF1 GEMM+GEGLU   h, W1 (repacked)      -> f [T][F] bf16
+//     FF2 GEMM                      f, W2                 -> h += .
+//   proj_out GEMM, transposed       W_out, h              -> y = NCHW(.) + x
+// The fp32 debug path runs the same schedule with fp32 buffers and kernels,
+// GEGLU as its own pass.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/st_block.h"
+#include "kernels.h"
+
+#define ST_API extern "C" __attribute__((visibility("default")))
+
+using namespace stb;
+
+namespace {
+
+thread_local std::string g_err;
+
+st_status fail(st_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+st_status hip_fail(hipError_t e, const char* what) {
+  return fail(ST_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
+
+struct LayerDev {
+  float* ln_w[3];
+  float* ln_b[3];
+  void* wqkv;  // [3C][C]: Wq1, Wk1, Wv1
+  float* bqkv;
+  void* wo1;
+  float* bo1;
+  void* wq2;
+  float* bq2;
+  void* wo2;
+  float* bo2;
+  void* w1;  // bf16: rows repacked in 64-row groups (32 value, 32 gate); fp32: as given
+  float* b1;  // [2F], original order
+  void* w2;
+  float* b2;
+};
+
+struct PendingTiming {
+  int kind;
+  hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct st_block {
+  int B, C, H, W, heads, D, depth;
+  st_dtype dtype;
+  bool bf16;
+  int N, T, F, npad, cpad;
+  size_t esz;
+  int device;
+  std::vector<void*> allocs;
+  size_t bytes_planned;
+  size_t bytes_cap;
+
+  float *gn_w, *gn_b;
+  void *w_in, *w_out;
+  float *b_in, *b_out;
+  std::vector<LayerDev> L;
+  void* wkv;  // [depth*2C][D]: per layer Wk2 rows then Wv2 rows
+  float* bkv;
+
+  float2 *gn_part, *gn_stats;
+  int gn_max_split;
+  void* u;
+  float* h;
+  void *q, *k, *vt, *o, *f;
+  float* z;  // fp32 path: FF1 output before GEGLU
+  void *kc, *vct;
+  long long ctx_layer_stride;
+
+  hipStream_t last_stream;
+  unsigned timing_mask;
+  std::vector<PendingTiming> pending;
+  std::vector<hipEvent_t> spare_events;
+};
+
+namespace {
+
+void* dalloc(st_block* b, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  bytes = static_cast<size_t>(round_up(static_cast<long long>(bytes), 256));
+  if (b->bytes_cap && b->bytes_planned + bytes > b->bytes_cap) return nullptr;
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  b->bytes_planned += bytes;
+  b->allocs.push_back(p);
+  return p;
+}
+
+void free_all(st_block* b) {
+  for (void* p : b->allocs) (void)hipFree(p);
+  b->allocs.clear();
+  for (auto& t : b->pending) {
+    (void)hipEventDestroy(t.e0);
+    (void)hipEventDestroy(t.e1);
+  }
+  b->pending.clear();
+  for (auto e : b->spare_events) (void)hipEventDestroy(e);
+  b->spare_events.clear();
+}
+
+// ------------------------------------------------------------ create helpers
+struct Creator {
+  st_block* b;
+  hipStream_t s;
+  st_status st = ST_OK;
+  std::string msg;
+
+  bool ok() const { return st == ST_OK; }
+  void oom(const char* what) {
+    if (ok()) { st = ST_ERR_OUT_OF_MEMORY; msg = std::string("out of device memory allocating ") + what; }
+  }
+  void dev(hipError_t e, const char* what) {
+    if (ok() && e != hipSuccess) { st = ST_ERR_DEVICE; msg = std::string(what) + ": " + hipGetErrorString(e); }
+  }
+  void* alloc(size_t bytes, const char* what) {
+    if (!ok()) return nullptr;
+    void* p = dalloc(b, bytes);
+    if (!p) oom(what);
+    return p;
+  }
+  // fp32 copy of a [n] vector given in the handle's dtype (NULL -> fill)
+  float* vec(const void* src, long long n, float fill, const char* what) {
+    float* d = static_cast<float*>(alloc(n * sizeof(float), what));
+    if (d) dev(to_f32(src, b->bf16, d, n, fill, s), what);
+    return d;
+  }
+  void vec_into(float* dst, const void* src, long long n, float fill, const char* what) {
+    if (ok()) dev(to_f32(src, b->bf16, dst, n, fill, s), what);
+  }
+  void copy(void* dst, const void* src, size_t bytes, const char* what) {
+    if (ok()) dev(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), what);
+  }
+  void* mat(const void* src, long long rows, long long cols, const char* what) {
+    void* d = alloc(rows * cols * b->esz, what);
+    copy(d, src, rows * cols * b->esz, what);
+    return d;
+  }
+  // bf16 path: weights that meet fp16 activations are kept as fp16 (exact
+  // within the fp16 range; larger magnitudes raise *overflow).
+  int* overflow = nullptr;
+  void to_f16(void* d, long long n, const char* what) {
+    if (ok() && b->bf16 && d) dev(bf16_to_f16_inplace(d, n, overflow, s), what);
+  }
+};
+
+}  // namespace
+
+// ======================================================================= ABI
+
+ST_API const char* st_last_error(void) { return g_err.c_str(); }
+
+ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
+                                 int D_ctx, int depth, st_dtype dtype,
+                                 const st_block_weights* w, void* stream,
+                                 st_block** out) {
+  g_err.clear();
+  if (!out) return fail(ST_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (B < 1 || H < 1 || W < 1) return fail(ST_ERR_INVALID, "B, H and W must be >= 1");
+  if (C < 64 || C % 64) return fail(ST_ERR_INVALID, "C must be a positive multiple of 64");
+  if (heads * 64 != C) return fail(ST_ERR_INVALID, "heads * 64 must equal C");
+  if (D_ctx < 64 || D_ctx % 64) return fail(ST_ERR_INVALID, "D_ctx must be a positive multiple of 64");
+  if (depth < 1) return fail(ST_ERR_INVALID, "depth must be >= 1");
+  if (dtype != ST_DTYPE_BF16 && dtype != ST_DTYPE_F32) return fail(ST_ERR_INVALID, "unknown dtype");
+  const long long N = static_cast<long long>(H) * W;
+  const long long T = N * B;
+  if (N > (1LL << 24) || T * 4LL * C > (1LL << 40))
+    return fail(ST_ERR_UNSUPPORTED, "token count too large");
+  if (!w) return fail(ST_ERR_INVALID, "weights are NULL");
+  if (!w->layers) return fail(ST_ERR_INVALID, "weights.layers is NULL");
+  auto need = [](const void* p) { return p != nullptr && aligned16(p); };
+  if (!need(w->proj_in_w) || !need(w->proj_out_w))
+    return fail(ST_ERR_INVALID, "proj_in_w / proj_out_w must be non-NULL and 16-byte aligned");
+  for (int l = 0; l < depth; ++l) {
+    const st_layer_weights& lw = w->layers[l];
+    const void* req[] = {lw.q1_w, lw.k1_w, lw.v1_w, lw.o1_w, lw.q2_w,
+                         lw.k2_w, lw.v2_w, lw.o2_w, lw.ff1_w, lw.ff2_w};
+    for (const void* p : req)
+      if (!need(p))
+        return fail(ST_ERR_INVALID, "layer " + std::to_string(l) +
+                                        ": every Linear weight must be non-NULL and 16-byte aligned");
+  }
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_fail(e, "hipGetDevice");
+  }
+
+  st_block* b = new (std::nothrow) st_block();
+  if (!b) return fail(ST_ERR_OUT_OF_MEMORY, "host allocation failed");
+  b->B = B; b->C = C; b->H = H; b->W = W; b->heads = heads; b->D = D_ctx; b->depth = depth;
+  b->dtype = dtype;
+  b->bf16 = dtype == ST_DTYPE_BF16;
+  b->N = static_cast<int>(N);
+  b->T = static_cast<int>(T);
+  b->F = 4 * C;
+  b->npad = static_cast<int>(round_up(N, 128));
+  b->cpad = 128;
+  b->esz = b->bf16 ? 2 : 4;
+  b->device = dev;
+  b->bytes_planned = 0;
+  b->bytes_cap = 0;
+  if (const char* cap = std::getenv("ST_MAX_DEVICE_BYTES")) b->bytes_cap = std::strtoull(cap, nullptr, 10);
+  b->last_stream = static_cast<hipStream_t>(stream);
+  b->timing_mask = 0;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Creator cr{b, s};
+  const long long CC = static_cast<long long>(C) * C;
+  const size_t es = b->esz;
+
+  // Block-level weights.
+  b->gn_w = cr.vec(w->gn_w, C, 1.f, "gn_w");
+  b->gn_b = cr.vec(w->gn_b, C, 0.f, "gn_b");
+  if (b->bf16) {
+    cr.overflow = static_cast<int*>(cr.alloc(sizeof(int), "overflow flag"));
+    if (cr.overflow) cr.dev(hipMemsetAsync(cr.overflow, 0, sizeof(int), s), "overflow flag");
+  }
+  b->w_in = cr.mat(w->proj_in_w, C, C, "proj_in_w");
+  cr.to_f16(b->w_in, CC, "proj_in_w to fp16");
+  b->b_in = cr.vec(w->proj_in_b, C, 0.f, "proj_in_b");
+  b->w_out = cr.mat(w->proj_out_w, C, C, "proj_out_w");
+  b->b_out = cr.vec(w->proj_out_b, C, 0.f, "proj_out_b");
+
+  // Context K/V weights of every layer in one matrix.
+  const long long kvrows = 2LL * C * depth;
+  b->wkv = cr.alloc(kvrows * D_ctx * es, "context K/V weights");
+  b->bkv = static_cast<float*>(cr.alloc(kvrows * sizeof(float), "context K/V biases"));
+
+  // GEGLU row map for the bf16 path (value/gate pairs in 64-row groups).
+  const int F = b->F;
+  int* d_map = nullptr;
+  if (b->bf16 && cr.ok()) {
+    std::vector<int> map(2 * F);
+    for (int p = 0; p < 2 * F; ++p) {
+      const int grp = p / 64, wi = p % 64;
+      map[p] = wi < 32 ? grp * 32 + wi : F + grp * 32 + (wi - 32);
+    }
+    d_map = static_cast<int*>(cr.alloc(map.size() * sizeof(int), "GEGLU row map"));
+    if (d_map) cr.dev(hipMemcpyAsync(d_map, map.data(), map.size() * sizeof(int),
+                                     hipMemcpyHostToDevice, s), "GEGLU row map");
+    if (cr.ok()) cr.dev(hipStreamSynchronize(s), "GEGLU row map");
+  }
+
+  b->L.resize(depth);
+  for (int l = 0; l < depth && cr.ok(); ++l) {
+    const st_layer_weights& lw = w->layers[l];
+    LayerDev& d = b->L[l];
+    const void* lnw[3] = {lw.ln1_w, lw.ln2_w, lw.ln3_w};
+    const void* lnb[3] = {lw.ln1_b, lw.ln2_b, lw.ln3_b};
+    for (int i = 0; i < 3; ++i) {
+      d.ln_w[i] = cr.vec(lnw[i], C, 1.f, "LayerNorm gamma");
+      d.ln_b[i] = cr.vec(lnb[i], C, 0.f, "LayerNorm beta");
+    }
+    d.wqkv = cr.alloc(3 * CC * es, "Q/K/V weights");
+    if (d.wqkv) {
+      cr.copy(d.wqkv, lw.q1_w, CC * es, "q1_w");
+      cr.copy(static_cast<char*>(d.wqkv) + CC * es, lw.k1_w, CC * es, "k1_w");
+      cr.copy(static_cast<char*>(d.wqkv) + 2 * CC * es, lw.v1_w, CC * es, "v1_w");
+      cr.to_f16(d.wqkv, 3 * CC, "Q/K/V weights to fp16");
+    }
+    d.bqkv = static_cast<float*>(cr.alloc(3LL * C * sizeof(float), "Q/K/V biases"));
+    if (d.bqkv) {
+      cr.vec_into(d.bqkv, lw.q1_b, C, 0.f, "q1_b");
+      cr.vec_into(d.bqkv + C, lw.k1_b, C, 0.f, "k1_b");
+      cr.vec_into(d.bqkv + 2 * C, lw.v1_b, C, 0.f, "v1_b");
+    }
+    d.wo1 = cr.mat(lw.o1_w, C, C, "o1_w");
+    d.bo1 = cr.vec(lw.o1_b, C, 0.f, "o1_b");
+    d.wq2 = cr.mat(lw.q2_w, C, C, "q2_w");
+    cr.to_f16(d.wq2, CC, "q2_w to fp16");
+    d.bq2 = cr.vec(lw.q2_b, C, 0.f, "q2_b");
+    d.wo2 = cr.mat(lw.o2_w, C, C, "o2_w");
+    d.bo2 = cr.vec(lw.o2_b, C, 0.f, "o2_b");
+    if (b->wkv && b->bkv) {
+      const long long r0 = 2LL * C * l;
+      const long long CD = static_cast<long long>(C) * D_ctx;
+      cr.copy(static_cast<char*>(b->wkv) + r0 * D_ctx * es, lw.k2_w, CD * es, "k2_w");
+      cr.copy(static_cast<char*>(b->wkv) + (r0 + C) * D_ctx * es, lw.v2_w, CD * es, "v2_w");
+      cr.vec_into(b->bkv + r0, lw.k2_b, C, 0.f, "k2_b");
+      cr.vec_into(b->bkv + r0 + C, lw.v2_b, C, 0.f, "v2_b");
+    }
+    d.w1 = cr.alloc(2LL * F * C * es, "ff1_w");
+    if (d.w1 && cr.ok()) {
+      if (b->bf16)
+        cr.dev(gather_rows(lw.ff1_w, d.w1, d_map, 2 * F, static_cast<long long>(C) * es, s), "ff1_w repack");
+      else
+        cr.copy(d.w1, lw.ff1_w, 2LL * F * C * es, "ff1_w");
+      cr.to_f16(d.w1, 2LL * F * C, "ff1_w to fp16");
+    }
+    d.b1 = cr.vec(lw.ff1_b, 2LL * F, 0.f, "ff1_b");
+    d.w2 = cr.mat(lw.ff2_w, C, F, "ff2_w");
+    cr.to_f16(d.w2, static_cast<long long>(C) * F, "ff2_w to fp16");
+    d.b2 = cr.vec(lw.ff2_b, C, 0.f, "ff2_b");
+  }
+
+  // Workspace.
+  b->gn_max_split = 64;
+  b->gn_part = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split, "GroupNorm partials"));
+  b->gn_stats = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS, "GroupNorm statistics"));
+  b->u = cr.alloc(T * C * es, "normalised activations");
+  b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
+  const long long headbuf = static_cast<long long>(B) * heads * b->npad * 64 * es;
+  b->q = cr.alloc(headbuf, "Q");
+  b->k = cr.alloc(headbuf, "K");
+  b->vt = cr.alloc(headbuf, "V^T");
+  b->o = cr.alloc(T * C * es, "attention output");
+  b->f = cr.alloc(T * F * es, "GEGLU output");
+  b->z = b->bf16 ? nullptr : static_cast<float*>(cr.alloc(T * 2LL * F * sizeof(float), "FF1 output"));
+  b->ctx_layer_stride = static_cast<long long>(B) * heads * b->cpad * 64;
+  b->kc = cr.alloc(b->ctx_layer_stride * depth * es, "context K");
+  b->vct = cr.alloc(b->ctx_layer_stride * depth * es, "context V^T");
+  // Padding rows of the per-head buffers are read by the attention kernels
+  // and must hold finite values; no kernel ever writes them.
+  if (cr.ok()) {
+    cr.dev(hipMemsetAsync(b->q, 0, headbuf, s), "clear Q");
+    cr.dev(hipMemsetAsync(b->k, 0, headbuf, s), "clear K");
+    cr.dev(hipMemsetAsync(b->vt, 0, headbuf, s), "clear V^T");
+    cr.dev(hipMemsetAsync(b->kc, 0, b->ctx_layer_stride * depth * es, s), "clear context K");
+    cr.dev(hipMemsetAsync(b->vct, 0, b->ctx_layer_stride * depth * es, s), "clear context V^T");
+  }
+  if (cr.ok()) cr.dev(hipStreamSynchronize(s), "create: synchronise");
+  if (cr.ok() && cr.overflow) {
+    int flag = 0;
+    cr.dev(hipMemcpy(&flag, cr.overflow, sizeof(int), hipMemcpyDeviceToHost), "overflow flag");
+    if (cr.ok() && flag) {
+      cr.st = ST_ERR_UNSUPPORTED;
+      cr.msg = "a projection weight exceeds the fp16 range (|w| > 65504)";
+    }
+  }
+  if (!cr.ok()) {
+    (void)hipStreamSynchronize(s);
+    (void)hipGetLastError();
+    free_all(b);
+    delete b;
+    return fail(cr.st, cr.msg);
+  }
+  *out = b;
+  return ST_OK;
+}
+
+namespace {
+
+hipEvent_t take_event(st_block* b) {
+  if (!b->spare_events.empty()) {
+    hipEvent_t e = b->spare_events.back();
+    b->spare_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+// Runs `launch` and, if its kind is selected, brackets it with events.
+template <class Fn>
+hipError_t run(st_block* b, int kind, hipStream_t s, Fn&& launch) {
+  if (!((b->timing_mask >> kind) & 1u)) return launch();
+  hipEvent_t e0 = take_event(b), e1 = take_event(b);
+  if (!e0 || !e1) {
+    if (e0) b->spare_events.push_back(e0);
+    if (e1) b->spare_events.push_back(e1);
+    return launch();
+  }
+  hipError_t r = hipEventRecord(e0, s);
+  if (r != hipSuccess) return r;
+  r = launch();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(e1, s);
+  b->pending.push_back({kind, e0, e1});
+  return r;
+}
+
+GemmParams gemm(const void* A, long long lda, const void* Bm, long long ldb,
+                int M, int N, int K, int kind) {
+  GemmParams p{};
+  p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb;
+  p.M = M; p.N = N; p.K = K;
+  p.epi.kind = kind;
+  return p;
+}
+
+#define ST_TRY(expr, what)                         \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
+                       int stop_stage, float* h_out, hipStream_t s) {
+  const bool bf = b->bf16;
+  const int B = b->B, C = b->C, N = b->N, T = b->T, F = b->F, D = b->D;
+  // 16-bit path operand types: fp16 where an activation produced by a norm
+  // or by GEGLU meets a weight, bf16 for attention outputs and the context.
+  const int act = bf ? ACT_F16 : ACT_F32;
+  auto G = [&](const GemmParams& p, int op, bool split) {
+    return bf ? gemm_mfma(p, op, split, s) : gemm_f32(p, s);
+  };
+
+  ST_TRY(run(b, ST_K_GN_STATS, s, [&] {
+           return gn_stats(x, bf, B, C, N, b->gn_part, b->gn_max_split, b->gn_stats, s);
+         }), "GroupNorm statistics");
+  ST_TRY(run(b, ST_K_PROJ_IN, s, [&] {
+           hipError_t e = gn_apply_tokens(x, bf, b->gn_stats, b->gn_w, b->gn_b, b->u, act, B, C, N, s);
+           if (e != hipSuccess) return e;
+           GemmParams p = gemm(b->u, C, b->w_in, C, T, C, C, EPI_STORE_F32);
+           p.epi.bias = b->b_in; p.epi.out_f32 = b->h; p.epi.ldo = C;
+           return G(p, ACT_F16, false);
+         }), "proj_in");
+  int stage = 0;
+  auto dump = [&]() -> bool { return stop_stage >= 0 && stage == stop_stage; };
+  if (dump()) {
+    ST_TRY(hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
+                          hipMemcpyDeviceToDevice, s), "stage copy");
+    return ST_OK;
+  }
+
+  ST_TRY(run(b, ST_K_CTX_KV, s, [&] {
+           GemmParams p = gemm(ctx, D, b->wkv, D, B * ST_CTX_LEN, 2 * C * b->depth, D, EPI_HEADS);
+           p.epi.bias = b->bkv;
+           p.epi.hs.dst[0] = b->kc; p.epi.hs.dst[1] = b->vct; p.epi.hs.dst[2] = nullptr;
+           p.epi.hs.transposed_mask = 2; p.epi.hs.nsplit = 2;
+           p.epi.hs.layer_stride = b->ctx_layer_stride;
+           p.epi.hs.rows_per_batch = ST_CTX_LEN; p.epi.hs.npad = b->cpad;
+           p.epi.hs.heads = b->heads; p.epi.hs.C = C;
+           return G(p, ACT_BF16, false);
+         }), "context K/V projection");
+
+  for (int l = 0; l < b->depth; ++l) {
+    const LayerDev& L = b->L[l];
+    // ---- self-attention sublayer
+    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+             return layernorm(b->h, L.ln_w[0], L.ln_b[0], b->u, act, T, C, s);
+           }), "LayerNorm 1");
+    ST_TRY(run(b, ST_K_QKV, s, [&] {
+             GemmParams p = gemm(b->u, C, L.wqkv, C, T, 3 * C, C, EPI_HEADS);
+             p.epi.bias = L.bqkv;
+             p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = b->k; p.epi.hs.dst[2] = b->vt;
+             p.epi.hs.transposed_mask = 4; p.epi.hs.nsplit = 3; p.epi.hs.layer_stride = 0;
+             p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
+             p.epi.hs.heads = b->heads; p.epi.hs.C = C;
+             return G(p, ACT_F16, false);
+           }), "Q/K/V projection");
+    ST_TRY(run(b, ST_K_SELF_ATTN, s, [&] {
+             AttnParams a{};
+             a.q = b->q; a.k = b->k; a.vt = b->vt; a.o = b->o;
+             a.B = B; a.heads = b->heads; a.C = C; a.Nq = N; a.Nk = N;
+             a.q_pad = b->npad; a.kv_pad = b->npad;
+             return bf ? attention_bf16(a, s) : attention_f32(a, s);
+           }), "self-attention");
+    ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
+             GemmParams p = gemm(b->o, C, L.wo1, C, T, C, C, EPI_RESID_F32);
+             p.epi.bias = L.bo1; p.epi.out_f32 = b->h; p.epi.ldo = C;
+             return G(p, ACT_BF16, false);
+           }), "self-attention out-projection");
+    ++stage;
+    if (dump()) break;
+    // ---- cross-attention sublayer
+    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+             return layernorm(b->h, L.ln_w[1], L.ln_b[1], b->u, act, T, C, s);
+           }), "LayerNorm 2");
+    ST_TRY(run(b, ST_K_CROSS_Q, s, [&] {
+             GemmParams p = gemm(b->u, C, L.wq2, C, T, C, C, EPI_HEADS);
+             p.epi.bias = L.bq2;
+             p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = nullptr; p.epi.hs.dst[2] = nullptr;
+             p.epi.hs.transposed_mask = 0; p.epi.hs.nsplit = 1; p.epi.hs.layer_stride = 0;
+             p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
+             p.epi.hs.heads = b->heads; p.epi.hs.C = C;
+             return G(p, ACT_F16, false);
+           }), "cross-attention Q projection");
+    ST_TRY(run(b, ST_K_CROSS_ATTN, s, [&] {
+             AttnParams a{};
+             a.q = b->q;
+             a.k = static_cast<const char*>(b->kc) + l * b->ctx_layer_stride * b->esz;
+             a.vt = static_cast<const char*>(b->vct) + l * b->ctx_layer_stride * b->esz;
+             a.o = b->o;
+             a.B = B; a.heads = b->heads; a.C = C; a.Nq = N; a.Nk = ST_CTX_LEN;
+             a.q_pad = b->npad; a.kv_pad = b->cpad;
+             return bf ? attention_bf16(a, s) : attention_f32(a, s);
+           }), "cross-attention");
+    ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
+             GemmParams p = gemm(b->o, C, L.wo2, C, T, C, C, EPI_RESID_F32);
+             p.epi.bias = L.bo2; p.epi.out_f32 = b->h; p.epi.ldo = C;
+             return G(p, ACT_BF16, false);
+           }), "cross-attention out-projection");
+    ++stage;
+    if (dump()) break;
+    // ---- feed-forward sublayer
+    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+             return layernorm(b->h, L.ln_w[2], L.ln_b[2], b->u, act, T, C, s);
+           }), "LayerNorm 3");
+    ST_TRY(run(b, ST_K_FF1_GEGLU, s, [&] {
+             if (bf) {
+               GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_GEGLU);
+               p.epi.bias = L.b1; p.epi.out_act = b->f; p.epi.F = F;
+               return gemm_mfma(p, ACT_F16, false, s);
+             }
+             GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_STORE_F32);
+             p.epi.bias = L.b1; p.epi.out_f32 = b->z; p.epi.ldo = 2 * F;
+             hipError_t e = gemm_f32(p, s);
+             if (e != hipSuccess) return e;
+             return geglu_f32(b->z, static_cast<float*>(b->f), T, F, s);
+           }), "feed-forward 1 + GEGLU");
+    ST_TRY(run(b, ST_K_FF2, s, [&] {
+             GemmParams p = gemm(b->f, F, L.w2, F, T, C, F, EPI_RESID_F32);
+             p.epi.bias = L.b2; p.epi.out_f32 = b->h; p.epi.ldo = C;
+             return G(p, ACT_F16, false);
+           }), "feed-forward 2");
+    ++stage;
+    if (dump()) break;
+  }
+  if (stop_stage >= 0) {
+    if (stage != stop_stage) return fail(ST_ERR_INVALID, "stage out of range");
+    ST_TRY(hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
+                          hipMemcpyDeviceToDevice, s), "stage copy");
+    return ST_OK;
+  }
+  ST_TRY(run(b, ST_K_PROJ_OUT, s, [&] {
+           // y^T orientation: rows = channels, columns = tokens, so the NCHW
+           // store is contiguous along tokens.
+           GemmParams p = gemm(b->w_out, C, b->h, C, C, T, C, EPI_NCHW);
+           p.epi.bias = b->b_out; p.epi.out_act = y; p.epi.resid_act = x;
+           p.epi.ntok = N; p.epi.ldo = C;
+           return G(p, ACT_BF16, true);
+         }), "proj_out");
+  return ST_OK;
+}
+
+bool overlaps(const void* a, size_t an, const void* c, size_t cn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), c0 = reinterpret_cast<uintptr_t>(c);
+  return a0 < c0 + cn && c0 < a0 + an;
+}
+
+st_status check_forward_args(st_block* b, const void* x, const void* ctx,
+                             const void* y) {
+  if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
+  if (!x || !ctx || !y) return fail(ST_ERR_INVALID, "x, ctx and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(ctx) || !aligned16(y))
+    return fail(ST_ERR_INVALID, "x, ctx and y must be 16-byte aligned");
+  const size_t xbytes = static_cast<size_t>(b->T) * b->C * b->esz;
+  const size_t cbytes = static_cast<size_t>(b->B) * ST_CTX_LEN * b->D * b->esz;
+  if (overlaps(y, xbytes, x, xbytes) || overlaps(y, xbytes, ctx, cbytes))
+    return fail(ST_ERR_INVALID, "y overlaps x or ctx");
+  return ST_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+ST_API st_status st_block_forward(st_block* b, const void* x, const void* ctx,
+                                  void* y, void* stream) {
+  g_err.clear();
+  st_status st = check_forward_args(b, x, ctx, y);
+  if (st != ST_OK) return st;
+  DeviceGuard g(b->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "select device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  b->last_stream = s;
+  return forward_impl(b, x, ctx, y, -1, nullptr, s);
+}
+
+ST_API st_status st_block_forward_stage(st_block* b, const void* x,
+                                        const void* ctx, int stage,
+                                        float* h_out, void* stream) {
+  g_err.clear();
+  if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
+  if (!x || !ctx || !h_out) return fail(ST_ERR_INVALID, "x, ctx and h_out must be non-NULL");
+  if (!aligned16(x) || !aligned16(ctx) || !aligned16(h_out))
+    return fail(ST_ERR_INVALID, "x, ctx and h_out must be 16-byte aligned");
+  if (stage < 0 || stage > 3 * b->depth) return fail(ST_ERR_INVALID, "stage out of range");
+  DeviceGuard g(b->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "select device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  b->last_stream = s;
+  return forward_impl(b, x, ctx, nullptr, stage, h_out, s);
+}
+
+ST_API void st_block_destroy(st_block* b) {
+  if (!b) return;
+  DeviceGuard g(b->device);
+  (void)hipStreamSynchronize(b->last_stream);
+  free_all(b);
+  delete b;
+}
+
+ST_API st_status st_block_set_timing(st_block* b, unsigned kind_mask) {
+  g_err.clear();
+  if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
+  b->timing_mask = kind_mask & ((1u << ST_K_COUNT) - 1u);
+  return ST_OK;
+}
+
+ST_API st_status st_block_read_timing(st_block* b, st_timing* out) {
+  g_err.clear();
+  if (!b || !out) return fail(ST_ERR_INVALID, "handle or out is NULL");
+  std::memset(out, 0, sizeof(*out));
+  st_status st = ST_OK;
+  for (auto& t : b->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventElapsedTime(&ms, t.e0, t.e1);
+    if (e != hipSuccess && st == ST_OK) st = hip_fail(e, "hipEventElapsedTime (stream not synchronised?)");
+    out->ms[t.kind] += ms;
+    out->launches[t.kind] += 1;
+    b->spare_events.push_back(t.e0);
+    b->spare_events.push_back(t.e1);
+  }
+  b->pending.clear();
+  return st;
+}

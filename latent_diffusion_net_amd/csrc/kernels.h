@@ -1,0 +1,110 @@
+// Host-side launch interface of the Spatial-Transformer block kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stb {
+
+// Element type of an activation buffer.
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1, ACT_F16 = 2 };
+
+enum EpiKind {
+  EPI_STORE_F32 = 0,  // out_f32[row*ldo + col] = acc + bias[col]
+  EPI_RESID_F32 = 1,  // out_f32[row*ldo + col] += acc + bias[col]
+  EPI_HEADS = 2,      // scatter into per-head Q/K (row-major) or V^T layouts
+  EPI_GEGLU = 3,      // paired value/gate columns -> value * GELU(gate), fp16 out
+  EPI_NCHW = 4        // rows = channels, cols = tokens: y = acc + bias[row] + x
+};
+
+// Destination of the head-split epilogue.  Column col of the product maps to
+// which = col / C, split s = which % nsplit, layer = which / nsplit, head =
+// (col % C) / 64, dim = col % 64; row maps to sample b = row / rows_per_batch
+// and sequence position n = row % rows_per_batch.  dst[s] + layer*layer_stride
+// is a [B*heads][npad][64] array, or [B*heads][64][npad] when bit s of
+// transposed_mask is set.
+struct HeadSplit {
+  void* dst[3];
+  int transposed_mask;
+  int nsplit;
+  long long layer_stride;
+  int rows_per_batch;
+  int npad;
+  int heads;
+  int C;
+};
+
+struct EpiParams {
+  int kind;
+  const float* bias;      // by column; by row for EPI_NCHW; may be NULL
+  float* out_f32;         // EPI_STORE_F32 / EPI_RESID_F32
+  int ldo;
+  void* out_act;          // EPI_GEGLU: [M][F]; EPI_NCHW: y [B][M][ntok]
+  const void* resid_act;  // EPI_NCHW: x [B][M][ntok]
+  int F;                  // EPI_GEGLU: value width
+  int ntok;               // EPI_NCHW: tokens per sample
+  HeadSplit hs;
+};
+
+// C[M][N] = A[M][K] * B[N][K]^T, then the epilogue.
+struct GemmParams {
+  const void* A;
+  long long lda;
+  const void* B;
+  long long ldb;
+  int M, N, K;
+  EpiParams epi;
+};
+
+// MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
+// ACT_F16 and gives the type of A and B.  With `b_split_f32`, B is fp32 in
+// memory and enters as two bf16 terms, hi = bf16(b) and lo = bf16(b - hi),
+// so that the product keeps about 16 significant bits of B (op must be
+// ACT_BF16).  Requires K % 64 == 0 and 16-byte aligned rows; any M, N.
+hipError_t gemm_mfma(const GemmParams& p, int op, bool b_split_f32,
+                     hipStream_t s);
+// fp32 everything (debug path).  Requires K % 16 == 0.
+hipError_t gemm_f32(const GemmParams& p, hipStream_t s);
+
+// Multi-head attention, per (b, head): O = softmax(Q K^T / 8) V.
+// q: [B*heads][q_pad][64], k: [B*heads][kv_pad][64], vt: [B*heads][64][kv_pad]
+// (padding rows must hold finite values), o: token-major [B*Nq][C].
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* o;
+  int B, heads, C;
+  int Nq, Nk;
+  int q_pad, kv_pad;
+};
+hipError_t attention_bf16(const AttnParams& p, hipStream_t s);
+hipError_t attention_f32(const AttnParams& p, hipStream_t s);
+int attention_bf16_q_tile();   // query rows per workgroup of the bf16 kernel
+int attention_bf16_kv_tile();  // key rows per LDS tile of the bf16 kernel
+
+// Norms and helpers.  `bf16` flags say whether activations are bf16 (else fp32).
+hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,
+                    float2* partial, int max_split, float2* stats,
+                    hipStream_t s);
+int gn_split(int C, int N, int max_split);
+// out: tokens [B*N][C] of type `out_type` (ACT_F32 or ACT_F16).
+hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* stats,
+                           const float* gamma, const float* beta, void* out,
+                           int out_type, int B, int C, int N, hipStream_t s);
+// u: [T][C] of type `out_type` (ACT_F32, ACT_BF16 or ACT_F16).
+hipError_t layernorm(const float* h, const float* gamma, const float* beta,
+                     void* u, int out_type, int T, int C, hipStream_t s);
+hipError_t geglu_f32(const float* z, float* f, long long T, int F,
+                     hipStream_t s);
+// dst[i] = float(src[i]) (src bf16 or fp32); src NULL -> dst[i] = fill.
+hipError_t to_f32(const void* src, bool bf16, float* dst, long long n,
+                  float fill, hipStream_t s);
+// In place: bf16 values -> fp16 (exact within the fp16 range; magnitudes
+// above 65504 set *overflow to 1).
+hipError_t bf16_to_f16_inplace(void* buf, long long n, int* overflow,
+                               hipStream_t s);
+// dst row r = src row map[r], rows of `row_bytes` bytes (multiple of 16).
+hipError_t gather_rows(const void* src, void* dst, const int* map, int rows,
+                       long long row_bytes, hipStream_t s);
+
+}  // namespace stb

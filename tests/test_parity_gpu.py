@@ -1,0 +1,213 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Tolerances.
+* bf16 storage (inputs, weights, output; 16-bit GEMM/attention operands with
+  fp32 accumulation): max-abs <= 3e-2 and rel-L2 <= 1e-2 on y.
+  The block's update Delta = y - x is far smaller than x (weights
+  N(0, 0.02^2)), so the update is checked as well, against a bound derived
+  from the arithmetic: storing y in bf16 (unit roundoff u = 2^-8) alone moves
+  Delta by up to u*|y| per element, and the 16-bit operands on the way to
+  Delta (about six roundings of relative size <= u each, partly cancelling)
+  add a few u of Delta itself, so
+      ||Delta_gpu - Delta_oracle|| <= u * (||y|| + 5 ||Delta||).
+* fp32 storage: rel-L2 <= 1e-5 on y; on Delta, fp32 sums of K <= 5120 terms
+  (u = 2^-24) give well under 1e-4.
+"""
+import gc
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.block as ob
+from latent_diffusion_net_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 3e-2
+BF16_REL_L2 = 1e-2
+U_BF16 = 2.0 ** -8
+F32_REL_L2 = 1e-5
+F32_DELTA_REL_L2 = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def run_gpu(cfg, inp, stages=()):
+    import torch
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    _say(f"[gpu] {cfg.name}: B={cfg.B} C={cfg.C} H={cfg.H} W={cfg.W} heads={cfg.heads} "
+         f"D_ctx={cfg.D_ctx} depth={cfg.depth} dtype={cfg.dtype}")
+    p = params_to_device(inp["params"], cfg.dtype)
+    x = array_to_device(inp["x"], cfg.dtype)
+    ctx = array_to_device(inp["ctx"], cfg.dtype)
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth,
+                  cfg.dtype, p)
+    del p
+    y = blk.forward(x, ctx)
+    hs = {s: blk.forward_stage(x, ctx, s) for s in stages}
+    torch.cuda.synchronize()
+    out = y.float().cpu().numpy().astype(np.float64)
+    hs = {s: h.cpu().numpy().astype(np.float64) for s, h in hs.items()}
+    blk.close()
+    return out, hs
+
+
+def check(cfg, inp, y, yo):
+    x = np.asarray(inp["x"], np.float64)
+    err = float(np.max(np.abs(y - yo)))
+    r = rel_l2(y, yo)
+    rd = rel_l2(y - x, yo - x)
+    _say(f"    max_abs={err:.3e} rel_l2={r:.3e} delta_rel_l2={rd:.3e}")
+    assert np.isfinite(y).all()
+    if cfg.dtype == "bf16":
+        assert err <= BF16_MAX_ABS, err
+        assert r <= BF16_REL_L2, r
+        bound = U_BF16 * (np.linalg.norm(yo) / np.linalg.norm(yo - x) + 5.0)
+        assert rd <= bound, (rd, bound)
+    else:
+        assert r <= F32_REL_L2, r
+        assert rd <= F32_DELTA_REL_L2, rd
+
+
+SMALL = [
+    # several 128-query tiles with a ragged tail (225 tokens), two layers
+    dict(name="b2_c128_15x15_d2", B=2, C=128, H=15, W=15, heads=2, D_ctx=128, depth=2),
+    # non-square map, three heads, wide context, ragged everything
+    dict(name="b1_c192_17x13_d1", B=1, C=192, H=17, W=13, heads=3, D_ctx=192, depth=1),
+    # one head, tokens a multiple of the tiles
+    dict(name="b2_c64_16x16_d1", B=2, C=64, H=16, W=16, heads=1, D_ctx=64, depth=1),
+    # degenerate: a single token (self-attention over one key)
+    dict(name="b1_c64_1x1_d2", B=1, C=64, H=1, W=1, heads=1, D_ctx=64, depth=2),
+    # C=320 (GEMM tiles ragged along N), 3 sublayers deep stack
+    dict(name="b1_c320_12x12_d3", B=1, C=320, H=12, W=12, heads=5, D_ctx=768, depth=3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s["name"])
+def test_small_stress(spec, dtype):
+    """Biases, norm affines and weights all drawn (every term matters)."""
+    spec = dict(spec)
+    cfg = synth.BlockConfig(spec.pop("name") + "_" + dtype, dtype=dtype, **spec)
+    inp = synth.make_inputs(cfg, 77, bias_std=0.05, norm_std=0.2)
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    y, _ = run_gpu(cfg, inp)
+    check(cfg, inp, y, yo)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sharp_softmax(dtype):
+    """Large weights: logits spread over tens of units, so the online softmax
+    rescales often and the row maxima matter."""
+    cfg = synth.BlockConfig("sharp_" + dtype, 1, 128, 20, 20, 2, 128, 1, dtype)
+    inp = synth.make_inputs(cfg, 5, weight_std=0.12)
+    yo, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
+                                 intermediates=True)
+    y, hs = run_gpu(cfg, inp, stages=(1, 2))
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for s, key in ((1, "l0_sa"), (2, "l0_ca")):
+        # the sublayer's own contribution, relative
+        prev = inter["h0"] if s == 1 else inter["l0_sa"]
+        r = rel_l2(hs[s] - prev, inter[key] - prev)
+        _say(f"    stage {s}: update rel_l2={r:.3e}")
+        assert r <= (tol if dtype == "bf16" else 1e-4), r
+    assert rel_l2(y, yo) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def test_stages_bf16():
+    """Residual stream after proj_in and after every sublayer."""
+    cfg = synth.BlockConfig("stages", 2, 128, 15, 15, 2, 128, 2, "bf16")
+    inp = synth.make_inputs(cfg, 9, bias_std=0.05, norm_std=0.2)
+    _, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
+                                intermediates=True)
+    keys = ["h0"] + [f"l{l}_{s}" for l in range(2) for s in ("sa", "ca", "ff")]
+    _, hs = run_gpu(cfg, inp, stages=range(len(keys)))
+    for s, key in enumerate(keys):
+        h = hs[s].reshape(inter[key].shape)
+        r = rel_l2(h, inter[key])
+        _say(f"    stage {s} ({key}): rel_l2={r:.3e}")
+        assert r <= 1e-2, (key, r)
+
+
+def test_f32_tiny_config_exact():
+    """The tiny fp32 workload at its full size, rel-L2 <= 1e-5."""
+    cfg = synth.CONFIGS[0]
+    inp = synth.make_inputs(cfg, synth.config_seed(0))
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    y, _ = run_gpu(cfg, inp)
+    check(cfg, inp, y, yo)
+
+
+def test_tiny_config_on_bf16_path():
+    """The tiny workload rounded to bf16 runs through the bf16 kernels too."""
+    c0 = synth.CONFIGS[0]
+    cfg = synth.BlockConfig(c0.name + "_as_bf16", c0.B, c0.C, c0.H, c0.W, c0.heads,
+                            c0.D_ctx, c0.depth, "bf16")
+    inp = synth.make_inputs(cfg, synth.config_seed(0))
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    y, _ = run_gpu(cfg, inp)
+    check(cfg, inp, y, yo)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_full_config(index):
+    """The workloads at their full sizes, every output element compared."""
+    cfg = synth.CONFIGS[index]
+    inp = synth.make_inputs(cfg, synth.config_seed(index))
+    y, _ = run_gpu(cfg, inp)
+    _say("    oracle ...")
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    check(cfg, inp, y, yo)
+    del inp, yo, y
+    gc.collect()
+
+
+def test_deterministic_and_timing():
+    import torch
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    cfg = synth.BlockConfig("det", 2, 128, 15, 15, 2, 128, 2, "bf16")
+    inp = synth.make_inputs(cfg, 3)
+    p = params_to_device(inp["params"], "bf16")
+    x = array_to_device(inp["x"], "bf16")
+    ctx = array_to_device(inp["ctx"], "bf16")
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    blk.set_timing(["self_attn", "cross_attn", "ff1_geglu"])
+    y1 = blk.forward(x, ctx)
+    y2 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    t = blk.read_timing()
+    assert t["self_attn"]["launches"] == 2 * cfg.depth
+    assert t["cross_attn"]["launches"] == 2 * cfg.depth
+    assert t["self_attn"]["ms"] > 0
+    assert "qkv" not in t
+    assert blk.read_timing() == {}
+    blk.close()
+
+
+def test_forward_rejects_aliasing_on_device():
+    import torch
+    from latent_diffusion_net_amd import STBlock, STError, array_to_device, params_to_device
+    cfg = synth.BlockConfig("alias", 1, 64, 4, 4, 1, 64, 1, "bf16")
+    inp = synth.make_inputs(cfg, 4)
+    p = params_to_device(inp["params"], "bf16")
+    x = array_to_device(inp["x"], "bf16")
+    ctx = array_to_device(inp["ctx"], "bf16")
+    blk = STBlock(1, 64, 4, 4, 1, 64, 1, "bf16", p)
+    with pytest.raises(STError, match="overlaps"):
+        blk.forward(x, ctx, y=x)
+    with pytest.raises(STError, match="stage"):
+        blk.forward_stage(x, ctx, 99)
+    torch.cuda.synchronize()
+    blk.close()
