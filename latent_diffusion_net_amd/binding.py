@@ -69,6 +69,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -m latent_diffusion_net_amd.build)")
+    # torch ships its own HIP runtime; load it first so that the library binds
+    # to that one instead of bringing a second runtime into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
     lib.st_block_create.argtypes = [i, i, i, i, i, i, i, i,

@@ -18,6 +18,8 @@
 //
 // fp32 path (debug builds): one thread per query row, K/V tiles in LDS,
 // online softmax in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,173 +27,300 @@ namespace stb {
 
 namespace {
 
-constexpr int QT = 128;  // query rows per workgroup
-constexpr int KT = 64;   // key rows per LDS tile
+constexpr int KT = 64;  // key rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy running max: a tile is exponentiated against the row's reference max
+// from earlier tiles; only when some lane's probabilities sum past this bound
+// (or overflow) is the exact max taken and the output rescaled.
+constexpr float kLazyBound = 256.f;
 
-__device__ __forceinline__ int kswz(int row, int chunk) {  // bf16 element offset
-  return row * 64 + ((chunk ^ (row & 7)) << 3);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// Both tiles live in LDS as 64 rows of 64 bf16 (128 bytes = eight 16-byte
+// chunks): K as [key][dim], V^T as [dim][key].  gfx950 serves a 16-byte LDS
+// read 16 lanes at a time over 64 banks (256 bytes), so two consecutive rows
+// fill the banks once; chunk c of row r is stored at c ^ ((r >> 1) & 7),
+// which gives the 16 rows of one read phase 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
+// Key order inside a K tile: LDS row r holds key perm(r), r with its bits 2
+// and 3 swapped.  Then the eight scores that the S^T accumulator layout gives
+// one lane for one PV step (rows 16st + 4*lhi + 0..3 and 16st + 8 + 4*lhi +
+// 0..3) are the keys 16st + 8*lhi + 0..7: contiguous in the V^T tile, so the
+// matching V^T operand is a single 16-byte read.
+__device__ __forceinline__ int perm(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * KT];  // [d][key]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// s_waitcnt that waits for vmcnt <= n only (lgkmcnt and expcnt at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup.
+// KIND only gives self- and cross-attention their own kernel symbols.
+template <int KIND, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(AttnParams p) {
+  constexpr int QW = 32 * QB;   // query rows per wavefront
+  constexpr int QT = QW * NW;   // query rows per workgroup
+  constexpr int BPW = 8 / NW;   // 1 KB DMA blocks of each 8 KB tile per wavefront
+  // Two K and two V^T buffers as distinct LDS objects, so that the compiler
+  // can tell the DMA into one buffer from the reads of the other and does
+  // not wait for the DMA before reading.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[KT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[KT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[64 * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * KT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
 
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+  // consecutive logical tiles (the same sample and head, hence the same K
+  // and V) are given to one XCD and share its L2.
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int qtiles = (p.Nq + QT - 1) / QT;
-  const int bh = blockIdx.x / qtiles;
-  const int qt = blockIdx.x - bh * qtiles;
+  const int bh = bid / qtiles;
+  const int qt = bid - bh * qtiles;
   const int b = bh / p.heads;
   const int head = bh - b * p.heads;
-  const int q0 = qt * QT + wave * 32;
+  const int q0 = qt * QT + wave * QW;
 
-  const bf16_t* Q = static_cast<const bf16_t*>(p.q) + static_cast<long long>(bh) * p.q_pad * 64;
-  const bf16_t* K = static_cast<const bf16_t*>(p.k) + static_cast<long long>(bh) * p.kv_pad * 64;
-  const bf16_t* VT = static_cast<const bf16_t*>(p.vt) + static_cast<long long>(bh) * 64 * p.kv_pad;
+  const uint16_t* Q = static_cast<const uint16_t*>(p.q) + static_cast<long long>(bh) * p.q_pad * 64;
+  const uint16_t* K = static_cast<const uint16_t*>(p.k) + static_cast<long long>(bh) * p.kv_pad * 64;
+  const uint16_t* VT = static_cast<const uint16_t*>(p.vt) + static_cast<long long>(bh) * 64 * p.kv_pad;
 
-  // Q^T as the B operand: lane holds query q0 + l32, dims 16s + 8*lhi + 0..7.
-  bf16x8 qf[4];
-  {
-    const int qrow = min(q0 + l32, p.q_pad - 1);
+  // Q^T as the B operand: block qb, step s -> query q0 + 32qb + l32,
+  // dims 16s + 8*lhi + 0..7.
+  uint4 qf[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = min(q0 + qb * 32 + l32, p.q_pad - 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Q + static_cast<long long>(qrow) * 64 + 16 * s + 8 * lhi);
+      qf[qb][s] = *reinterpret_cast<const uint4*>(Q + static_cast<long long>(qrow) * 64 + 16 * s + 8 * lhi);
   }
 
-  // Tile loads: K tile 64 rows x 8 chunks, V^T tile 64 rows (dims) x 8 chunks.
-  uint4 rk[2], rv[2];
-  auto load_tile = [&](int t) {
-    const int k0 = t * KT;
+  // Tiles move to LDS with global_load_lds_dwordx4: one instruction moves 64
+  // lanes x 16 bytes into 1 KB of LDS (8 rows), lane i landing in slot i, so
+  // each lane fetches the chunk that belongs in its slot.
+  int koff[BPW], voff[BPW];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int q = tid + 256 * r;
-      const int row = q >> 3, c = q & 7;
-      rk[r] = *reinterpret_cast<const uint4*>(K + static_cast<long long>(k0 + row) * 64 + c * 8);
-      rv[r] = *reinterpret_cast<const uint4*>(VT + static_cast<long long>(row) * p.kv_pad + k0 + c * 8);
-    }
+  for (int j2 = 0; j2 < BPW; ++j2) {
+    const int r = 8 * (wave * BPW + j2) + (lane >> 3);
+    const int cl = (lane & 7) ^ ((r >> 1) & 7);
+    koff[j2] = perm(r) * 64 + cl * 8;
+    voff[j2] = r * p.kv_pad + cl * 8;
+  }
+  auto issue_k = [&](int t, uint16_t* dst) {
+    const uint16_t* src = K + static_cast<long long>(t) * KT * 64;
+#pragma unroll
+    for (int j2 = 0; j2 < BPW; ++j2)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + koff[j2]),
+                                       (lds_ptr_t)(dst + (wave * BPW + j2) * 512), 16, 0, 0);
   };
-  auto store_tile = [&](int buf) {
+  auto issue_v = [&](int t, uint16_t* dst) {
+    const uint16_t* src = VT + t * KT;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int q = tid + 256 * r;
-      const int row = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(&sK[buf][kswz(row, c)]) = rk[r];
-      *reinterpret_cast<uint4*>(&sV[buf][kswz(row, c)]) = rv[r];
-    }
+    for (int j2 = 0; j2 < BPW; ++j2)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + voff[j2]),
+                                       (lds_ptr_t)(dst + (wave * BPW + j2) * 512), 16, 0, 0);
   };
 
-  floatx16 o[2];
+  floatx16 o[QB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < QB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;  // this lane's partial row sum (its 32 of every 64 keys)
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
+  float mref[QB], lsum[QB];  // lsum: this lane's partial row sums
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
   const float c = 0.125f * kLog2e;
-
   const int ntiles = (p.Nk + KT - 1) / KT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
 
-    // S^T block kb: keys kb*32 + 8*(r/4) + 4*lhi + r%4, query l32.
-    floatx16 sc[2];
+  // S^T = K Q^T for one tile; sc[qb][kb] entry r: tile row
+  // kb*32 + 8*(r/4) + 4*lhi + r%4 (key perm of it), query q0 + 32qb + l32.
+  auto qk = [&](const uint16_t* kbuf, floatx16 (&sc)[QB][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][kswz(kb * 32 + l32, 2 * s + lhi)]);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
-      }
-    }
-    const int kvalid = p.Nk - t * KT;
-    if (kvalid < KT) {
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          if (key >= kvalid) sc[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kbuf + swz(kb * 32 + l32, 2 * s + lhi));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sc[qb][kb] = mfma32x32x16(a, qf[qb][s], sc[qb][kb], bf16_t{});
+      }
+  };
+
+  // Exact row max of the tile: raises the reference max and rescales the
+  // running sum and output.
+  auto exact_max = [&](floatx16 (&sc)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mt = sc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[qb][kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(mref[qb], mt);
+      const float alpha = __builtin_amdgcn_exp2f((mref[qb] - m_new) * c);
+      mref[qb] = m_new;
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+    }
+  };
+  // Probabilities of a tile against the reference max, as packed bf16 B
+  // operands: step st takes entries r = 8*(st%2) + 0..7 of block st/2 (keys
+  // 16st + 8*lhi + 0..7).  Returns true if some lane's probabilities sum past
+  // the lazy bound (or overflow), i.e. the reference max must be raised.
+  auto exponentiate = [&](const floatx16 (&sc)[QB][2], uint4 (&pb)[QB][4],
+                          float (&ps)[QB]) -> bool {
+    bool big = false;
+    bf16x2 one;
+    one[0] = static_cast<__bf16>(1.0f);
+    one[1] = static_cast<__bf16>(1.0f);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mc = mref[qb] * c;
+      ps[qb] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x2 pk;
+          pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[qb][st >> 1][8 * (st & 1) + 2 * j], c, -mc)));
+          pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[qb][st >> 1][8 * (st & 1) + 2 * j + 1], c, -mc)));
+          ps[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ps[qb], false);
+          w[j] = __builtin_bit_cast(uint32_t, pk);
+        }
+        pb[qb][st] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      big |= !(ps[qb] <= kLazyBound);
+    }
+    return big;
+  };
+
+  // O^T += V^T P^T.  V^T operand of dim block db, step st: row db*32 + l32,
+  // keys 16st + 8*lhi + 0..7 (chunk 2st + lhi): the keys of the P^T operand,
+  // in the same order (see perm).
+  auto pv = [&](const uint16_t* vbuf, const uint4 (&pb)[QB][4]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const uint4 a = *reinterpret_cast<const uint4*>(vbuf + swz(db * 32 + l32, 2 * st + lhi));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = mfma32x32x16(a, pb[qb][st], o[qb][db], bf16_t{});
+      }
+  };
+
+  // Keys at or beyond Nk in tile t (the last tile when Nk % KT != 0) -> -inf.
+  auto mask_tile = [&](int t, floatx16 (&sc)[QB][2]) {
+    const int kvalid = p.Nk - t * KT;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (perm(kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) >= kvalid) sc[qb][kb][r] = -INFINITY;
+  };
+
+  // Software pipeline over key tiles.  Iteration t holds S_t in registers,
+  // computes S_{t+1} on the matrix cores while the vector units exponentiate
+  // S_t, then adds P_t V_t.  Tile j of K and of V^T lives in buffer j % 2;
+  // iteration t reads K_{t+1} and V_t while the DMA of K_{t+2} and V_{t+1}
+  // is in flight.  The MFMAs of S_{t+1} and the exponentials of S_t form one
+  // branch-free block that the scheduler can interleave; the exact max of
+  // tile 0 is taken in the prologue and a ragged last tile is masked as soon
+  // as its scores exist.
+  const int ragged_last = (p.Nk % KT) ? ntiles - 1 : -1;
+  floatx16 sa[QB][2], sb[QB][2];
+  issue_k(0, sK0);
+  issue_v(0, sV0);
+  if (ntiles > 1) issue_k(1, sK1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  qk(sK0, sa);
+  if (ragged_last == 0) mask_tile(0, sa);
+  exact_max(sa);
+  __syncthreads();  // every wavefront is done with K_0 before K_2 replaces it
+
+  auto iter = [&](int t, floatx16 (&scur)[QB][2], floatx16 (&snext)[QB][2],
+                  const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
+    if (t + 2 < ntiles) issue_k(t + 2, kw);
+    if (t + 1 < ntiles) issue_v(t + 1, vw);
+    // S_{t+1} (unused past the last tile: its LDS buffer then holds stale,
+    // finite data) and P_t.
+    qk(kn, snext);
+    uint4 pb[QB][4];
+    float ps[QB];
+    if (__any(exponentiate(scur, pb, ps))) {  // rare
+      exact_max(scur);
+      exponentiate(scur, pb, ps);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
+    if (t + 1 == ragged_last) mask_tile(t + 1, snext);
+    pv(vc, pb);
+    wait_vmcnt<0>();  // K_{t+2} and V_{t+1} have landed
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    iter(t, sa, sb, sK1, sV0, sK0, sV1);
+    if (t + 1 < ntiles) iter(t + 1, sb, sa, sK0, sV1, sK1, sV0);
+  }
+
+  // Row sums over both lane halves, normalise, store O[token][head*64 + d].
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = lsum[qb] + __shfl_xor(lsum[qb], 32, 64);
+    const float inv = 1.0f / l_tot;
+    const int qrow = q0 + qb * 32 + l32;
+    if (qrow < p.Nq) {
+      uint16_t* orow = static_cast<uint16_t*>(p.o) +
+                       (static_cast<long long>(b) * p.Nq + qrow) * p.C + head * 64;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * lhi;
+          const uint2 pk = make_uint2(pack2bf(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
+                                      pack2bf(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv));
+          *reinterpret_cast<uint2*>(orow + d) = pk;
         }
     }
-    float mt = sc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
-    m_run = m_new;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -mc));
-        sc[kb][r] = e;
-        ls += e;
-      }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-
-    // P^T operand of step st (keys 16st..16st+15 of the tile): this lane's
-    // keys 16st + 4*lhi + 0..3 and 16st + 8 + 4*lhi + 0..3, i.e. accumulator
-    // entries r = 8*(st%2) + 0..7 of block st/2.
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8 pb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(sc[st >> 1][8 * (st & 1) + j]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // V^T operand: dim row i*32 + l32, the same eight keys in the same order.
-        const int drow = i * 32 + l32;
-        const int key0 = 16 * st + 4 * lhi;        // 4 keys, 8 bytes
-        const int key1 = 16 * st + 8 + 4 * lhi;    // 4 keys, 8 bytes
-        const bf16_t* vrow = &sV[buf][0];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kswz(drow, key0 >> 3) + (key0 & 7));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kswz(drow, key1 >> 3) + (key1 & 7));
-        const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[i], 0, 0, 0);
-      }
-    }
-
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Row sum over both lane halves, normalise, store O[token][head*64 + d].
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-  const int qrow = q0 + l32;
-  if (qrow < p.Nq) {
-    bf16_t* orow = static_cast<bf16_t*>(p.o) +
-                   (static_cast<long long>(b) * p.Nq + qrow) * p.C + head * 64;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = i * 32 + 8 * g + 4 * lhi;
-        const uint2 pk = make_uint2(pack2bf(o[i][4 * g] * inv, o[i][4 * g + 1] * inv),
-                                    pack2bf(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + d) = pk;
-      }
   }
 }
+
+#ifndef ST_ATTN_QB
+#define ST_ATTN_QB 1
+#endif
+#ifndef ST_ATTN_NW
+#define ST_ATTN_NW 4
+#endif
+constexpr int kQB = ST_ATTN_QB, kNW = ST_ATTN_NW;
+constexpr int kQT = 32 * kQB * kNW;
 
 // ---------------------------------------------------------------- fp32 path
 constexpr int FQ = 64;   // queries per workgroup (one per thread)
@@ -244,12 +373,17 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(AttnParams p) {
 
 }  // namespace
 
-int attention_bf16_q_tile() { return QT; }
+int attention_bf16_q_tile() { return kQT; }
 int attention_bf16_kv_tile() { return KT; }
 
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
-  const int qtiles = (p.Nq + QT - 1) / QT;
-  attn_bf16_kernel<<<p.B * p.heads * qtiles, 256, 0, s>>>(p);
+  const int qtiles = (p.Nq + kQT - 1) / kQT;
+  if (p.q_pad < qtiles * kQT || p.kv_pad < ((p.Nk + KT - 1) / KT) * KT)
+    return hipErrorInvalidValue;  // padded buffers must cover every tile
+  if (p.Nk == kCtxLen)
+    attn_bf16_kernel<1, kQB, kNW><<<p.B * p.heads * qtiles, 64 * kNW, 0, s>>>(p);
+  else
+    attn_bf16_kernel<0, kQB, kNW><<<p.B * p.heads * qtiles, 64 * kNW, 0, s>>>(p);
   return hipGetLastError();
 }
 
