@@ -77,6 +77,24 @@ __device__ __forceinline__ float gelu_erf(float g) {
   return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
 }
 
+// The same GELU with erf from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 +
+// t a5)))) exp(-x^2), t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7; odd in
+// x.  Used where the result is rounded to a 16-bit type, whose rounding
+// (>= 2^-12 relative) is far larger than that error.
+__device__ __forceinline__ float gelu_as(float g) {
+  const float x = fabsf(g) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.0f);
+  return 0.5f * g * (1.0f + copysignf(erf_abs, g));
+}
+
 // 32x32x16 MFMA with fp32 accumulation, bf16 or fp16 operands (8 per lane).
 __device__ __forceinline__ floatx16 mfma32x32x16(const uint4& a, const uint4& b,
                                                  floatx16 c, bf16_t) {
@@ -87,6 +105,25 @@ __device__ __forceinline__ floatx16 mfma32x32x16(const uint4& a, const uint4& b,
                                                  floatx16 c, f16_t) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// s_waitcnt that waits for vmcnt <= n and for every LDS access of this
+// wavefront (lgkmcnt 0), expcnt left at its maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the release fence of __syncthreads(), which
+// would wait for every outstanding global load -- including the LDS DMA of
+// later pipeline stages.  Callers wait for exactly what they need first
+// (wait_vmcnt_lds).  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace stb

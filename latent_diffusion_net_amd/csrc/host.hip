@@ -206,8 +206,10 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   if (dtype != ST_DTYPE_BF16 && dtype != ST_DTYPE_F32) return fail(ST_ERR_INVALID, "unknown dtype");
   const long long N = static_cast<long long>(H) * W;
   const long long T = N * B;
-  if (N > (1LL << 24) || T * 4LL * C > (1LL << 40))
-    return fail(ST_ERR_UNSUPPORTED, "token count too large");
+  // Kernels index activations with 32-bit element offsets: the largest
+  // buffer, the GEGLU output [T][4C], must stay below 2^31 elements.
+  if (N > (1LL << 24) || T * 4LL * C >= (1LL << 31))
+    return fail(ST_ERR_UNSUPPORTED, "B*H*W*4*C must stay below 2^31");
   if (!w) return fail(ST_ERR_INVALID, "weights are NULL");
   if (!w->layers) return fail(ST_ERR_INVALID, "weights.layers is NULL");
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };

@@ -54,13 +54,6 @@ __device__ __forceinline__ int perm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// s_waitcnt that waits for vmcnt <= n only (lgkmcnt and expcnt at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup.
 // KIND only gives self- and cross-attention their own kernel symbols.
 template <int KIND, int QB, int NW>
@@ -283,8 +276,8 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
     if (t + 1 == ragged_last) mask_tile(t + 1, snext);
     pv(vc, pb);
-    wait_vmcnt<0>();  // K_{t+2} and V_{t+1} have landed
-    __syncthreads();
+    wait_vmcnt_lds<0>();  // K_{t+2} and V_{t+1} have landed
+    stage_barrier();
   };
   for (int t = 0; t < ntiles; t += 2) {
     iter(t, sa, sb, sK1, sV0, sK0, sV1);

@@ -1,15 +1,21 @@
 // GEMMs of the Spatial-Transformer block: C[M][N] = A[M][K] * B[N][K]^T with
 // both operands K-contiguous (activations [tokens][in], weights [out][in]).
 //
-// 16-bit path: v_mfma_f32_32x32x16_{bf16,f16} on gfx950.  A 256-thread workgroup
-// owns a 128x128 output tile; each of its four wavefronts owns a 64x64
-// quarter as 2x2 MFMA blocks of 32x32 (64 fp32 accumulators per lane).  K
-// advances 64 at a time through two LDS buffers: the next tile's global loads
-// are issued before the current tile's MFMAs and written to the other buffer
-// after them, so one barrier per K step suffices.  LDS rows are 128 bytes
-// (64 bf16); the eight 16-byte chunks of a row are XOR-swizzled by the row
-// index so that the 32 rows one MFMA operand read touches spread over all
-// banks.  Rows beyond M or N are clamped on load and masked on store.
+// 16-bit operands (bf16 or fp16) on v_mfma_f32_32x32x16 with fp32
+// accumulation.  A 256-thread workgroup owns a 128x128 output tile; each of
+// its four wavefronts owns a 64x64 quarter as 2x2 MFMA blocks of 32x32 (64
+// fp32 accumulators per lane).  K advances 32 at a time through a ring of
+// four LDS stages filled by global_load_lds_dwordx4 (no staging registers),
+// so three stages are in flight while one is consumed, with one barrier per
+// stage.  Each stage buffer is its own LDS object: the compiler can then
+// tell a DMA into one stage from reads of another and does not wait on it.
+// LDS rows are 64 bytes (32 elements, four 16-byte chunks); chunk c of row r
+// is stored at c ^ ((r >> 2) & 3), which spreads the 16 rows of one
+// 16-lane read phase over all 16 bank groups of gfx950's 64-bank LDS.  Rows
+// beyond M or N are clamped on load and masked on store.
+//
+// B given as fp32 (the residual stream entering proj_out) goes through a
+// register-staged variant that splits each value into two bf16 terms.
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
@@ -24,8 +30,9 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 
+// 128-byte rows (64 elements): chunk c of row r at c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 // One 8-element chunk of B.  SPLIT: B is fp32 and the chunk holds its bf16
@@ -47,6 +54,240 @@ __device__ __forceinline__ uint4 load_b_chunk(const void* B, long long ldb,
   } else {
     return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(B) +
                                            row * ldb + k);
+  }
+}
+
+// Head-split store of four consecutive rows (tokens) of one column.  For a
+// V^T destination the four values are contiguous and go out as one 8-byte
+// store when they belong to one sample and stay aligned.
+__device__ __forceinline__ void store_heads4(const HeadSplit& hs, int row0,
+                                             int col, const float v[4],
+                                             float bias, int M) {
+  const int which = col / hs.C;
+  const int s = which % hs.nsplit;
+  const int layer = which / hs.nsplit;
+  const int within = col - which * hs.C;
+  const int head = within >> 6;
+  const int dim = within & 63;
+  bf16_t* base = static_cast<bf16_t*>(hs.dst[s]) + layer * hs.layer_stride;
+  const bool trans = (hs.transposed_mask >> s) & 1;
+  const int b0 = row0 / hs.rows_per_batch;
+  const int n0 = row0 - b0 * hs.rows_per_batch;
+  if (trans && (hs.rows_per_batch & 3) == 0 && row0 + 3 < M) {
+    const long long bh = static_cast<long long>(b0) * hs.heads + head;
+    const uint2 pk = make_uint2(pack2bf(v[0] + bias, v[1] + bias),
+                                pack2bf(v[2] + bias, v[3] + bias));
+    *reinterpret_cast<uint2*>(base + (bh * kHeadDim + dim) * hs.npad + n0) = pk;
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = row0 + k;
+    if (row >= M) break;
+    const int b = row / hs.rows_per_batch;
+    const int n = row - b * hs.rows_per_batch;
+    const long long bh = static_cast<long long>(b) * hs.heads + head;
+    const long long idx = trans ? (bh * kHeadDim + dim) * hs.npad + n
+                                : (bh * hs.npad + n) * kHeadDim + dim;
+    base[idx] = f2bf(v[k] + bias);
+  }
+}
+
+// Epilogue through LDS.  The wavefront's 64x64 fp32 tile is written to a
+// 16 KB LDS area in the accumulator layout, then read back along whichever
+// axis is contiguous in the destination, so every global access is a 8- or
+// 16-byte vector on consecutive addresses (rows of h, rows of a head of Q/K,
+// runs of tokens of V^T and of an NCHW plane, rows of the GEGLU output).
+// Column col of the tile is stored at col ^ (32 * ((row >> 2) & 1)): the
+// two lane halves of an accumulator write (rows 4 apart) then use opposite
+// bank halves.  Requires N % 64 == 0 except for the NCHW kind (tokens).
+__device__ __forceinline__ int stg(int row, int col) {
+  return row * 64 + (col ^ (((row >> 2) & 1) << 5));
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p,
+                                             const floatx16 (&acc)[2][2],
+                                             int m0, int n0, int wm, int wn,
+                                             int lane, float* stage) {
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int M = p.M, N = p.N;
+  const int R0 = m0 + wm * 64, C0 = n0 + wn * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[stg(i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3), j * 32 + l32)] = acc[i][j][r];
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
+  if (C0 >= N || R0 >= M) return;
+
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32) {
+    // lane -> 4 consecutive columns of one row; 4 rows per pass
+    const int lc = (lane & 15) * 4;
+    const float4 bias = p.epi.bias ? *reinterpret_cast<const float4*>(p.epi.bias + C0 + lc)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    // all 16 residual rows are loaded before the first store (the compiler
+    // cannot prove a store to h disjoint from the next row's load)
+    float4 hin[16];
+    if constexpr (EPI == EPI_RESID_F32) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = R0 + it * 4 + (lane >> 4);
+        hin[it] = row < M ? *reinterpret_cast<const float4*>(
+                                p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int lr = it * 4 + (lane >> 4);
+      const int row = R0 + lr;
+      if (row >= M) break;
+      const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+      float4 v = make_float4(c.x + bias.x, c.y + bias.y, c.z + bias.z, c.w + bias.w);
+      if constexpr (EPI == EPI_RESID_F32) {
+        v.x += hin[it].x; v.y += hin[it].y; v.z += hin[it].z; v.w += hin[it].w;
+      }
+      *reinterpret_cast<float4*>(p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = v;
+    }
+  } else if constexpr (EPI == EPI_GEGLU) {
+    // columns 0..31 are values, 32..63 the matching gates; output
+    // f[row][(C0 / 64) * 32 + 0..31] in fp16; lane -> 4 outputs of one row
+    const int F = p.epi.F;
+    const int fc0 = (C0 >> 6) * 32;
+    const int lc = (lane & 7) * 4;
+    float bv[4], bg[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bv[k] = p.epi.bias ? p.epi.bias[fc0 + lc + k] : 0.f;
+      bg[k] = p.epi.bias ? p.epi.bias[F + fc0 + lc + k] : 0.f;
+    }
+    f16_t* out = static_cast<f16_t*>(p.epi.out_act);
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int lr = it * 8 + (lane >> 3);
+      const int row = R0 + lr;
+      if (row >= M) break;
+      const float4 v = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+      const float4 g = *reinterpret_cast<const float4*>(&stage[stg(lr, 32 + lc)]);
+      const uint2 pk = make_uint2(
+          pack2h((v.x + bv[0]) * gelu_as(g.x + bg[0]), (v.y + bv[1]) * gelu_as(g.y + bg[1])),
+          pack2h((v.z + bv[2]) * gelu_as(g.z + bg[2]), (v.w + bv[3]) * gelu_as(g.w + bg[3])));
+      *reinterpret_cast<uint2*>(out + static_cast<long long>(row) * F + fc0 + lc) = pk;
+    }
+  } else if constexpr (EPI == EPI_HEADS) {
+    // The 64 columns are one head of one split (C0 and C are multiples of
+    // 64).
+    const HeadSplit& hs = p.epi.hs;
+    const int which = C0 / hs.C;
+    const int sp = which % hs.nsplit;
+    const int layer = which / hs.nsplit;
+    const int head = (C0 - which * hs.C) >> 6;
+    bf16_t* base = static_cast<bf16_t*>(hs.dst[sp]) + layer * hs.layer_stride;
+    const float* bias = p.epi.bias ? p.epi.bias + C0 : nullptr;
+    if (!((hs.transposed_mask >> sp) & 1)) {
+      // [bh][n][64]: lane -> 4 consecutive dims of one token
+      const int lc = (lane & 15) * 4;
+      float bb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bb[k] = bias ? bias[lc + k] : 0.f;
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int lr = it * 4 + (lane >> 4);
+        const int row = R0 + lr;
+        if (row >= M) break;
+        const int b = row / hs.rows_per_batch;
+        const int n = row - b * hs.rows_per_batch;
+        const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+        const uint2 pk = make_uint2(pack2bf(c.x + bb[0], c.y + bb[1]), pack2bf(c.z + bb[2], c.w + bb[3]));
+        const long long bh = static_cast<long long>(b) * hs.heads + head;
+        *reinterpret_cast<uint2*>(base + (bh * hs.npad + n) * kHeadDim + lc) = pk;
+      }
+    } else {
+      // V^T [bh][64][npad]: lane -> one dim, 4 consecutive tokens
+      const int dim = lane;
+      const float bb = bias ? bias[dim] : 0.f;
+      const bool vec = (hs.rows_per_batch & 3) == 0;
+#pragma unroll 2
+      for (int it = 0; it < 16; ++it) {
+        const int lr0 = it * 4;
+        const int row0 = R0 + lr0;
+        if (row0 >= M) break;
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = stage[stg(lr0 + k, dim)] + bb;
+        if (vec && row0 + 3 < M) {
+          const int b = row0 / hs.rows_per_batch;
+          const int n = row0 - b * hs.rows_per_batch;
+          const long long bh = static_cast<long long>(b) * hs.heads + head;
+          *reinterpret_cast<uint2*>(base + (bh * kHeadDim + dim) * hs.npad + n) =
+              make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = row0 + k;
+            if (row >= M) break;
+            const int b = row / hs.rows_per_batch;
+            const int n = row - b * hs.rows_per_batch;
+            const long long bh = static_cast<long long>(b) * hs.heads + head;
+            base[(bh * kHeadDim + dim) * hs.npad + n] = f2bf(v[k]);
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_NCHW) {
+    // rows = channels, columns = tokens: y[b][c][n] = acc + bias[c] + x[b][c][n];
+    // lane -> 4 consecutive tokens of one channel
+    const int ntok = p.epi.ntok;
+    const int lc = (lane & 15) * 4;
+    const bf16_t* xin = static_cast<const bf16_t*>(p.epi.resid_act);
+    bf16_t* yout = static_cast<bf16_t*>(p.epi.out_act);
+    const int t0 = C0 + lc;
+    const int b0 = t0 / ntok;
+    const int nn = t0 - b0 * ntok;
+    const bool vec = (ntok & 3) == 0 && t0 + 3 < N;
+    const long long base0 = static_cast<long long>(b0) * p.epi.ldo * ntok + nn;
+    if (vec) {
+      // all 16 input runs are loaded before the first store
+      uint2 xv[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int c = R0 + it * 4 + (lane >> 4);
+        xv[it] = c < M ? *reinterpret_cast<const uint2*>(xin + base0 + static_cast<long long>(c) * ntok)
+                       : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int lr = it * 4 + (lane >> 4);
+        const int c = R0 + lr;
+        if (c >= M) break;
+        const float bias = p.epi.bias ? p.epi.bias[c] : 0.f;
+        const float4 a = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+        const float y0 = a.x + bias + __uint_as_float(xv[it].x << 16);
+        const float y1 = a.y + bias + __uint_as_float(xv[it].x & 0xffff0000u);
+        const float y2 = a.z + bias + __uint_as_float(xv[it].y << 16);
+        const float y3 = a.w + bias + __uint_as_float(xv[it].y & 0xffff0000u);
+        *reinterpret_cast<uint2*>(yout + base0 + static_cast<long long>(c) * ntok) =
+            make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
+      }
+    } else {
+      for (int it = 0; it < 16; ++it) {
+        const int lr = it * 4 + (lane >> 4);
+        const int c = R0 + lr;
+        if (c >= M) break;
+        const float bias = p.epi.bias ? p.epi.bias[c] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = t0 + k;
+          if (t >= N) break;
+          const int b = t / ntok;
+          const long long off = (static_cast<long long>(b) * p.epi.ldo + c) * ntok + (t - b * ntok);
+          yout[off] = f2bf(stage[stg(lr, lc + k)] + bias + bf2f(xin[off]));
+        }
+      }
+    }
   }
 }
 
@@ -124,44 +365,139 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // Accumulator layout of a 32x32 block: lane holds column (lane & 31) and
-  // rows 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
-  if constexpr (EPI == EPI_GEGLU) {
-    // Repacked W1: each group of 64 rows is 32 value rows then the 32
-    // matching gate rows, so block j=0 holds values and j=1 their gates.
-    const int pc0 = n0 + wn * 64;
-    if (pc0 < N) {
-      const int fcol = (pc0 >> 6) * 32 + l32;
-      const int F = p.epi.F;
-      const float bv = p.epi.bias ? p.epi.bias[fcol] : 0.f;
-      const float bg = p.epi.bias ? p.epi.bias[F + fcol] : 0.f;
-      f16_t* out = static_cast<f16_t*>(p.epi.out_act);
+  // every wavefront is done reading the stage buffers before they hold
+  // the epilogue tiles
+  stage_barrier();
+  float* stage = reinterpret_cast<float*>(wave == 0 ? &sA[0][0] : wave == 1 ? &sA[1][0]
+                                          : wave == 2 ? &sB[0][0] : &sB[1][0]);
+  epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
+}
+
+// ------------------------------------------------------- DMA-ring GEMM
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// Stage rows of BKT elements: 64 (128 bytes, eight chunks, chunk c of row r
+// at c ^ ((r >> 1) & 7)) or 32 (64 bytes, four chunks, at c ^ ((r >> 2) &
+// 3)); either way the 16 rows of one 16-lane read phase cover all 16 bank
+// groups of the 64-bank LDS.
+template <int BKT>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  if constexpr (BKT == 64)
+    return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+  else
+    return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+template <int EPI, typename OpT, int BKT, int NST>
+__global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
+  // NST stage buffers per operand, each its own LDS object (see the file
+  // comment); unused ones are never referenced and take no LDS.
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[BM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[BM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[BM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[BN * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[BN * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[BN * BKT];
+  static_assert(NST == 2 || NST == 3, "stages");
+  constexpr int RPB = 1024 / (BKT * 2);      // rows per 1 KB DMA block
+  constexpr int DPW = BM / RPB / 4;          // DMA blocks per wave per operand per stage
+  constexpr int CPR = BKT / 8;               // 16-byte chunks per row
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N;
+  const uint16_t* A = static_cast<const uint16_t*>(p.A);
+  const uint16_t* Bm = static_cast<const uint16_t*>(p.B);
+  const int l32 = lane & 31, lhi = lane >> 5;
+
+  // Lane i of a DMA block lands in slot i: row i / CPR, physical chunk
+  // i % CPR, so it fetches the logical chunk that belongs there.
+  long long aoff[DPW], boff[DPW];
+#pragma unroll
+  for (int j2 = 0; j2 < DPW; ++j2) {
+    const int row = RPB * (wave * DPW + j2) + lane / CPR;
+    const int pc = lane % CPR;
+    const int cl = (BKT == 64) ? (pc ^ ((row >> 1) & 7)) : (pc ^ ((row >> 2) & 3));
+    aoff[j2] = static_cast<long long>(min(m0 + row, M - 1)) * p.lda + cl * 8;
+    boff[j2] = static_cast<long long>(min(n0 + row, N - 1)) * p.ldb + cl * 8;
+  }
+  auto issue = [&](int k, uint16_t* sa, uint16_t* sb) {
+#pragma unroll
+    for (int j2 = 0; j2 < DPW; ++j2) {
+      const int blk = (wave * DPW + j2) * 512;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(A + aoff[j2] + k * BKT),
+                                       (lds_ptr_t)(sa + blk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bm + boff[j2] + k * BKT),
+                                       (lds_ptr_t)(sb + blk), 16, 0, 0);
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+#pragma unroll
+    for (int s = 0; s < BKT / 16; ++s) {
+      const int chunk = 2 * s + lhi;
+      uint4 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const uint4*>(sa + swz_k<BKT>(wm * 64 + i * 32 + l32, chunk));
+        b[i] = *reinterpret_cast<const uint4*>(sb + swz_k<BKT>(wn * 64 + i * 32 + l32, chunk));
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          if (row < M) {
-            const float v = acc[i][0][r] + bv;
-            const float g = acc[i][1][r] + bg;
-            out[static_cast<long long>(row) * F + fcol] = static_cast<f16_t>(v * gelu_erf(g));
-          }
-        }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j], OpT{});
+    }
+  };
+
+  // Iteration k: stage k must have landed (later stages may still be in
+  // flight), every wavefront must be past iteration k-1 (whose buffer is
+  // refilled now with stage k + NST - 1), then stage k is consumed.
+  const int nk = p.K / BKT;
+  constexpr int PER = 2 * DPW;  // DMA instructions per stage per wavefront
+  issue(0, sA0, sB0);
+  if (nk > 1 && NST > 2) issue(1, sA1, sB1);
+  auto step = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa,
+                  uint16_t* wb) {
+    if constexpr (NST == 3) {
+      if (k + 1 < nk) wait_vmcnt_lds<PER>();
+      else wait_vmcnt_lds<0>();
+    } else {
+      wait_vmcnt_lds<0>();
+    }
+    stage_barrier();
+    if (k + NST - 1 < nk) issue(k + NST - 1, wa, wb);
+    compute(ca, cb);
+  };
+  if constexpr (NST == 3) {
+    for (int k = 0; k < nk; k += 3) {
+      step(k, sA0, sB0, sA2, sB2);
+      if (k + 1 < nk) step(k + 1, sA1, sB1, sA0, sB0);
+      if (k + 2 < nk) step(k + 2, sA2, sB2, sA1, sB1);
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + l32;
-        if (col >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          if (row < M) epi_store<EPI, bf16_t>(p.epi, row, col, acc[i][j][r]);
-        }
-      }
+    for (int k = 0; k < nk; k += 2) {
+      step(k, sA0, sB0, sA1, sB1);
+      if (k + 1 < nk) step(k + 1, sA1, sB1, sA0, sB0);
+    }
   }
+
+  // every wavefront is done reading the stage buffers before they hold
+  // the epilogue tiles
+  stage_barrier();
+  float* stage = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1);
+  epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
 }
 
 // ---------------------------------------------------------------- fp32 GEMM
@@ -211,37 +547,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 
 }  // namespace
 
+#ifndef ST_GEMM_BKT
+#define ST_GEMM_BKT 64
+#endif
+#ifndef ST_GEMM_NST
+#define ST_GEMM_NST 2
+#endif
+constexpr int kBKT = ST_GEMM_BKT, kNST = ST_GEMM_NST;
+
 hipError_t gemm_mfma(const GemmParams& p, int op, bool b_split_f32,
                      hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.K % BK) return hipErrorInvalidValue;
-  if (b_split_f32 && op != ACT_BF16) return hipErrorInvalidValue;
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
+  if (b_split_f32) {
+    if (op != ACT_BF16 || p.epi.kind != EPI_NCHW) return hipErrorInvalidValue;
+    gemm_mfma_kernel<EPI_NCHW, bf16_t, true><<<grid, kThreads, 0, s>>>(p);
+    return hipGetLastError();
+  }
+#define ST_GEMM_CASE(E)                                                     \
+  case E:                                                                   \
+    if (op == ACT_F16) gemm_dma_kernel<E, f16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p); \
+    else gemm_dma_kernel<E, bf16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p);           \
+    break;
   switch (p.epi.kind) {
-    case EPI_STORE_F32:
-      if (op == ACT_F16) gemm_mfma_kernel<EPI_STORE_F32, f16_t, false><<<grid, kThreads, 0, s>>>(p);
-      else gemm_mfma_kernel<EPI_STORE_F32, bf16_t, false><<<grid, kThreads, 0, s>>>(p);
-      break;
-    case EPI_RESID_F32:
-      if (op == ACT_F16) gemm_mfma_kernel<EPI_RESID_F32, f16_t, false><<<grid, kThreads, 0, s>>>(p);
-      else gemm_mfma_kernel<EPI_RESID_F32, bf16_t, false><<<grid, kThreads, 0, s>>>(p);
-      break;
-    case EPI_HEADS:
-      if (op == ACT_F16) gemm_mfma_kernel<EPI_HEADS, f16_t, false><<<grid, kThreads, 0, s>>>(p);
-      else gemm_mfma_kernel<EPI_HEADS, bf16_t, false><<<grid, kThreads, 0, s>>>(p);
-      break;
-    case EPI_GEGLU:
-      if (op == ACT_F16) gemm_mfma_kernel<EPI_GEGLU, f16_t, false><<<grid, kThreads, 0, s>>>(p);
-      else gemm_mfma_kernel<EPI_GEGLU, bf16_t, false><<<grid, kThreads, 0, s>>>(p);
-      break;
-    case EPI_NCHW:
-      if (b_split_f32) gemm_mfma_kernel<EPI_NCHW, bf16_t, true><<<grid, kThreads, 0, s>>>(p);
-      else if (op == ACT_F16) gemm_mfma_kernel<EPI_NCHW, f16_t, false><<<grid, kThreads, 0, s>>>(p);
-      else gemm_mfma_kernel<EPI_NCHW, bf16_t, false><<<grid, kThreads, 0, s>>>(p);
-      break;
+    ST_GEMM_CASE(EPI_STORE_F32)
+    ST_GEMM_CASE(EPI_RESID_F32)
+    ST_GEMM_CASE(EPI_HEADS)
+    ST_GEMM_CASE(EPI_GEGLU)
+    ST_GEMM_CASE(EPI_NCHW)
     default:
       return hipErrorInvalidValue;
   }
+#undef ST_GEMM_CASE
   return hipGetLastError();
 }
 
