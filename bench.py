@@ -15,8 +15,11 @@ the host as `cpu_baseline`.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +28,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "spatial-transformer block tokens/s + attention TFLOP/s (% bf16 MFMA peak)"
+ATTN_SRC = os.path.join(ROOT, "latent_diffusion_net_amd", "csrc", "k_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "self_attn_sdxl_down1_hbm_traffic.md")
+COPY_BYTES = 256 << 20      # calibration copy: 256 MiB read + 256 MiB written
+SELF_ATTN_KERNEL = "attn_bf16_kernel<0,"   # kernel-name prefix of self-attention
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 DEFAULT_WORKLOAD = 3       # index into synth.CONFIGS: SDXL Down1, 64x64, depth 2
 
@@ -40,6 +47,52 @@ def block_flops(cfg) -> float:
     per_layer = 36.0 * T * C * C + attention_flops(cfg) + 4.0 * B * N * 77 * C \
         + 4.0 * B * 77 * D * C
     return 4.0 * T * C * C + depth * per_layer
+
+
+def source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per self-attention launch from the committed counter summary,
+    or None when that summary was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel source sha256\[:16\]: ([0-9a-f]{16})", txt)
+    b = re.search(r"traffic_bytes_per_launch: ([0-9.eE+]+)", txt)
+    if not h or not b or h.group(1) != source_hash():
+        return None
+    return float(b.group(1))
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Counter CSVs of two rocprofv3 --pmc passes over `bench.py --pmc-pass`
+    -> per-launch HBM bytes of self-attention, scaled by the copy kernel."""
+    def vals(path, counter, pred):
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter and pred(r["Kernel_Name"])]
+
+    def avg(v):
+        return (sum(v) / len(v), len(v)) if v else (float("nan"), 0)
+    is_attn = lambda k: SELF_ATTN_KERNEL in k
+    # the calibration copy is by far the largest copyBuffer dispatch (the
+    # others copy weights while the block is created)
+    is_copy = lambda k: "copyBuffer" in k
+    fa, na = avg(vals(fetch_csv, "FETCH_SIZE", is_attn))
+    fc, nc = max(vals(fetch_csv, "FETCH_SIZE", is_copy) or [float("nan")]), 1
+    wa, _ = avg(vals(write_csv, "WRITE_SIZE", is_attn))
+    wc = max(vals(write_csv, "WRITE_SIZE", is_copy) or [float("nan")])
+    kf = COPY_BYTES / (fc * 1024.0)  # counters are in KiB
+    kw = COPY_BYTES / (wc * 1024.0)
+    fetch_b = fa * 1024.0 * kf
+    write_b = wa * 1024.0 * kw
+    return {"attn_fetch_kib": fa, "attn_write_kib": wa, "copy_fetch_kib": fc,
+            "copy_write_kib": wc, "fetch_scale": kf, "write_scale": kw,
+            "attn_launches": na, "copy_launches": nc,
+            "traffic_bytes_per_launch": fetch_b + write_b,
+            "fetch_bytes": fetch_b, "write_bytes": write_b}
 
 
 def cpu_baseline(cfg, inp):
@@ -69,10 +122,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="also time every kernel kind in an extra untimed pass")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="counter-collection run: a 256 MiB device copy (the "
+                         "calibration kernel) then a few forwards; no JSON")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the self-attention HBM traffic from two "
+                         "counter CSVs of --pmc-pass runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        r = summarize_pmc(*args.summarize_pmc)
+        r["kernel_source_sha256_16"] = source_hash()
+        print(json.dumps(r, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the block is not sharded across GPUs in this build.", file=sys.stderr)
+              "the block runs on one GPU and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -94,6 +158,17 @@ def main():
     for _ in range(args.warmup):
         blk.forward(x, ctx, y, stream)
     torch.cuda.synchronize()
+    if args.pmc_pass:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            blk.forward(x, ctx, y, stream)
+        torch.cuda.synchronize()
+        blk.close()
+        print("pmc pass done", flush=True)
+        return
     blk.read_timing()
     blk.set_timing(["self_attn"])
 
@@ -142,7 +217,8 @@ def main():
                    "depth": cfg.depth, "tokens_per_step": cfg.T},
         "roofline": {"bound": "mfma", "achieved": attn_tflops,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel (self-attention)",
                      "us_per_launch": attn_s * 1e6,
                      "flops_per_launch": attention_flops(cfg)},
