@@ -56,7 +56,10 @@ def build(verbose: bool = False) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    # --no-undefined: a kernel whose host stub was not emitted fails here,
+    # not when the library is loaded
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined",
+          "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 

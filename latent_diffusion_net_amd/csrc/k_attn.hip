@@ -35,7 +35,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyBound = 256.f;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+// Word 3 of a gfx9 buffer resource for raw (untyped) dword access.
+constexpr int kBufferWord3 = 0x00020000;
+
+// buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes from `base` + soff + voff
+// (reads at or past nbytes return 0) into the 1 KB of LDS at `lds`, lane i
+// landing in slot i.
+__device__ __forceinline__ void tile_dma(const void* base, int nbytes, uint16_t* lds,
+                                         unsigned voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
 
 // Both tiles live in LDS as 64 rows of 64 bf16 (128 bytes = eight 16-byte
 // chunks): K as [key][dim], V^T as [dim][key].  gfx950 serves a 16-byte LDS
@@ -61,13 +72,15 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   constexpr int QW = 32 * QB;   // query rows per wavefront
   constexpr int QT = QW * NW;   // query rows per workgroup
   constexpr int BPW = 8 / NW;   // 1 KB DMA blocks of each 8 KB tile per wavefront
-  // Two K and two V^T buffers as distinct LDS objects, so that the compiler
-  // can tell the DMA into one buffer from the reads of the other and does
-  // not wait for the DMA before reading.
+  // Three K and three V^T buffers as distinct LDS objects, so that the
+  // compiler can tell the DMA into one buffer from the reads of the others
+  // and does not wait for the DMA before reading.
   __shared__ __attribute__((aligned(16))) uint16_t sK0[KT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[KT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sK2[KT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[64 * KT];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[64 * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t sV2[64 * KT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -100,30 +113,29 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
       qf[qb][s] = *reinterpret_cast<const uint4*>(Q + static_cast<long long>(qrow) * 64 + 16 * s + 8 * lhi);
   }
 
-  // Tiles move to LDS with global_load_lds_dwordx4: one instruction moves 64
-  // lanes x 16 bytes into 1 KB of LDS (8 rows), lane i landing in slot i, so
-  // each lane fetches the chunk that belongs in its slot.
-  int koff[BPW], voff[BPW];
+  // Tiles move to LDS with tile_dma: one instruction moves 8 rows, so each
+  // lane fetches the chunk that belongs in its slot.  The buffer covers this
+  // (sample, head)'s K or V^T, the tile's offset is a scalar and each lane
+  // adds a fixed 32-bit offset, so nothing per tile lives in vector
+  // registers.
+  const int kv_bytes = p.kv_pad * 128;  // K or V^T of one (sample, head)
+  unsigned koff[BPW], voff[BPW];
 #pragma unroll
   for (int j2 = 0; j2 < BPW; ++j2) {
     const int r = 8 * (wave * BPW + j2) + (lane >> 3);
     const int cl = (lane & 7) ^ ((r >> 1) & 7);
-    koff[j2] = perm(r) * 64 + cl * 8;
-    voff[j2] = r * p.kv_pad + cl * 8;
+    koff[j2] = static_cast<unsigned>(perm(r) * 64 + cl * 8) * 2u;
+    voff[j2] = static_cast<unsigned>(r * p.kv_pad + cl * 8) * 2u;
   }
   auto issue_k = [&](int t, uint16_t* dst) {
-    const uint16_t* src = K + static_cast<long long>(t) * KT * 64;
 #pragma unroll
     for (int j2 = 0; j2 < BPW; ++j2)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + koff[j2]),
-                                       (lds_ptr_t)(dst + (wave * BPW + j2) * 512), 16, 0, 0);
+      tile_dma(K, kv_bytes, dst + (wave * BPW + j2) * 512, koff[j2], t * KT * 128);
   };
   auto issue_v = [&](int t, uint16_t* dst) {
-    const uint16_t* src = VT + t * KT;
 #pragma unroll
     for (int j2 = 0; j2 < BPW; ++j2)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + voff[j2]),
-                                       (lds_ptr_t)(dst + (wave * BPW + j2) * 512), 16, 0, 0);
+      tile_dma(VT, kv_bytes, dst + (wave * BPW + j2) * 512, voff[j2], t * KT * 2);
   };
 
   floatx16 o[QB][2];
@@ -137,6 +149,20 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
   const float c = 0.125f * kLog2e;
+  // Byte offset of this lane's operand chunk for step s within a 32-row half
+  // tile; rows 32..63 add 4096 bytes (the swizzle key depends on row bits 1-3
+  // only).  The empty asm hides how the offset is formed, so that the buffer
+  // base and the half-tile step become the read's immediate offset instead
+  // of one address register per buffer.
+  unsigned lo[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    lo[s4] = static_cast<unsigned>(swz(l32, 2 * s4 + lhi)) * 2u;
+    asm volatile("" : "+v"(lo[s4]));
+  }
+  auto lds_operand = [&](const uint16_t* buf, int half, int s4) -> uint4 {
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(buf) + half * 4096 + lo[s4]);
+  };
   const int ntiles = (p.Nk + KT - 1) / KT;
 
   // S^T = K Q^T for one tile; sc[qb][kb] entry r: tile row
@@ -152,7 +178,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kbuf + swz(kb * 32 + l32, 2 * s + lhi));
+        const uint4 a = lds_operand(kbuf, kb, s);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[qb][kb] = mfma32x32x16(a, qf[qb][s], sc[qb][kb], bf16_t{});
@@ -220,7 +246,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const uint4 a = *reinterpret_cast<const uint4*>(vbuf + swz(db * 32 + l32, 2 * st + lhi));
+        const uint4 a = lds_operand(vbuf, db, st);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = mfma32x32x16(a, pb[qb][st], o[qb][db], bf16_t{});
@@ -228,8 +254,11 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   };
 
   // Keys at or beyond Nk in tile t (the last tile when Nk % KT != 0) -> -inf.
+  // The bound is hidden from the compiler so that the comparisons stay here
+  // instead of being hoisted out of the loop into 32 live masks.
   auto mask_tile = [&](int t, floatx16 (&sc)[QB][2]) {
-    const int kvalid = p.Nk - t * KT;
+    int kvalid = p.Nk - t * KT;
+    asm volatile("" : "+s"(kvalid));
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -239,50 +268,59 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
           if (perm(kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) >= kvalid) sc[qb][kb][r] = -INFINITY;
   };
 
-  // Software pipeline over key tiles.  Iteration t holds S_t in registers,
-  // computes S_{t+1} on the matrix cores while the vector units exponentiate
-  // S_t, then adds P_t V_t.  Tile j of K and of V^T lives in buffer j % 2;
-  // iteration t reads K_{t+1} and V_t while the DMA of K_{t+2} and V_{t+1}
-  // is in flight.  The MFMAs of S_{t+1} and the exponentials of S_t form one
-  // branch-free block that the scheduler can interleave; the exact max of
-  // tile 0 is taken in the prologue and a ragged last tile is masked as soon
-  // as its scores exist.
+  // Software pipeline over key tiles.  Iteration t turns S_t into P_t on the
+  // vector units, computes S_{t+1} in the registers that S_t held, then adds
+  // P_t V_t.  Tile j of K and of V^T lives in buffer j % 3: iteration t reads
+  // K_{t+1} and V_t, K_{t+2} and V_{t+1} are in flight, and it issues the DMA
+  // of K_{t+3} and V_{t+2}, so that every tile has two iterations to arrive.
+  // The exact max of tile 0 is taken in the prologue and a ragged last tile
+  // is masked as soon as its scores exist.
   const int ragged_last = (p.Nk % KT) ? ntiles - 1 : -1;
-  floatx16 sa[QB][2], sb[QB][2];
+  floatx16 sc[QB][2];  // S_t
   issue_k(0, sK0);
   issue_v(0, sV0);
-  if (ntiles > 1) issue_k(1, sK1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  qk(sK0, sa);
-  if (ragged_last == 0) mask_tile(0, sa);
-  exact_max(sa);
-  __syncthreads();  // every wavefront is done with K_0 before K_2 replaces it
+  if (ntiles > 1) { issue_k(1, sK1); issue_v(1, sV1); }
+  if (ntiles > 2) issue_k(2, sK2);
+  wait_vmcnt_lds<0>();
+  stage_barrier();
+  qk(sK0, sc);
+  if (ragged_last == 0) mask_tile(0, sc);
+  exact_max(sc);
+  stage_barrier();  // every wavefront is done with K_0 before K_3 replaces it
 
-  auto iter = [&](int t, floatx16 (&scur)[QB][2], floatx16 (&snext)[QB][2],
-                  const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
-    if (t + 2 < ntiles) issue_k(t + 2, kw);
-    if (t + 1 < ntiles) issue_v(t + 1, vw);
-    // S_{t+1} (unused past the last tile: its LDS buffer then holds stale,
-    // finite data) and P_t.
-    qk(kn, snext);
+  constexpr int kIssued = 2 * BPW;  // DMA instructions per wavefront per iteration
+  auto iter = [&](int t, const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
+    if (t + 3 < ntiles) issue_k(t + 3, kw);
+    if (t + 2 < ntiles) issue_v(t + 2, vw);
     uint4 pb[QB][4];
     float ps[QB];
-    if (__any(exponentiate(scur, pb, ps))) {  // rare
-      exact_max(scur);
-      exponentiate(scur, pb, ps);
+    if (__any(exponentiate(sc, pb, ps))) {  // rare
+      exact_max(sc);
+      exponentiate(sc, pb, ps);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
-    if (t + 1 == ragged_last) mask_tile(t + 1, snext);
+    // S_{t+1} (unused past the last tile: its LDS buffer then holds stale,
+    // finite data)
+    qk(kn, sc);
+    if (t + 1 == ragged_last) mask_tile(t + 1, sc);
     pv(vc, pb);
-    wait_vmcnt_lds<0>();  // K_{t+2} and V_{t+1} have landed
+    // K_{t+2} and V_{t+1} have landed (loads complete in order, so at most
+    // this iteration's own DMA is still in flight)
+    if (t + 3 < ntiles) wait_vmcnt_lds<kIssued>();
+    else wait_vmcnt_lds<0>();
     stage_barrier();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    iter(t, sa, sb, sK1, sV0, sK0, sV1);
-    if (t + 1 < ntiles) iter(t + 1, sb, sa, sK0, sV1, sK1, sV0);
+  // Unrolled by the buffer period, so that every buffer is a distinct LDS
+  // object at each use; whole periods first, then up to two tail tiles.
+  int t = 0;
+  for (; t + 3 <= ntiles; t += 3) {
+    iter(t, sK1, sV0, sK0, sV2);
+    iter(t + 1, sK2, sV1, sK1, sV0);
+    iter(t + 2, sK0, sV2, sK2, sV1);
   }
+  if (t < ntiles) iter(t, sK1, sV0, sK0, sV2);
+  if (t + 1 < ntiles) iter(t + 1, sK2, sV1, sK1, sV0);
 
   // Row sums over both lane halves, normalise, store O[token][head*64 + d].
 #pragma unroll
