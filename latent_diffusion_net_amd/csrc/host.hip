@@ -17,7 +17,8 @@
 //     out-projection GEMM           O, Wo2                -> h += .
 //     LayerNorm 3, FF1 GEMM+GEGLU   h, W1 (repacked)      -> f [T][F] bf16
 //     FF2 GEMM                      f, W2                 -> h += .
-//   proj_out GEMM, transposed       W_out, h              -> y = NCHW(.) + x
+//   proj_out GEMM, transposed       [W_out|W_out], h hi|lo -> y = NCHW(.) + x
+//     (the last FF2 also writes h as bf16 hi + lo terms, [T][2C])
 // The fp32 debug path runs the same schedule with fp32 buffers and kernels,
 // GEGLU as its own pass.
 #include <hip/hip_runtime.h>
@@ -91,7 +92,7 @@ struct st_block {
   size_t bytes_cap;
 
   float *gn_w, *gn_b;
-  void *w_in, *w_out;
+  void *w_in, *w_out;  // bf16 path: w_out is [C][2C], the weight twice along K
   float *b_in, *b_out;
   std::vector<LayerDev> L;
   void* wkv;  // [depth*2C][D]: per layer Wk2 rows then Wv2 rows
@@ -101,6 +102,7 @@ struct st_block {
   int gn_max_split;
   void* u;
   float* h;
+  void* hsplit;  // bf16 path: [T][2C] bf16, h = hi + lo (hi in [0,C), lo in [C,2C))
   void *q, *k, *vt, *o, *f;
   float* z;  // fp32 path: FF1 output before GEGLU
   void *kc, *vct;
@@ -265,7 +267,16 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->w_in = cr.mat(w->proj_in_w, C, C, "proj_in_w");
   cr.to_f16(b->w_in, CC, "proj_in_w to fp16");
   b->b_in = cr.vec(w->proj_in_b, C, 0.f, "proj_in_b");
-  b->w_out = cr.mat(w->proj_out_w, C, C, "proj_out_w");
+  if (b->bf16) {
+    // [W_out | W_out]: proj_out multiplies it with [h_hi | h_lo] (K = 2C)
+    b->w_out = cr.alloc(2 * CC * es, "proj_out_w");
+    for (int half = 0; half < 2 && cr.ok(); ++half)
+      cr.dev(hipMemcpy2DAsync(static_cast<char*>(b->w_out) + half * C * es, 2 * C * es,
+                              w->proj_out_w, C * es, C * es, C, hipMemcpyDeviceToDevice, s),
+             "proj_out_w");
+  } else {
+    b->w_out = cr.mat(w->proj_out_w, C, C, "proj_out_w");
+  }
   b->b_out = cr.vec(w->proj_out_b, C, 0.f, "proj_out_b");
 
   // Context K/V weights of every layer in one matrix.
@@ -346,6 +357,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->gn_stats = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS, "GroupNorm statistics"));
   b->u = cr.alloc(T * C * es, "normalised activations");
   b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
+  b->hsplit = b->bf16 ? cr.alloc(T * 2LL * C * es, "split residual stream") : nullptr;
   const long long headbuf = static_cast<long long>(B) * heads * b->npad * 64 * es;
   b->q = cr.alloc(headbuf, "Q");
   b->k = cr.alloc(headbuf, "K");
@@ -442,8 +454,8 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   // 16-bit path operand types: fp16 where an activation produced by a norm
   // or by GEGLU meets a weight, bf16 for attention outputs and the context.
   const int act = bf ? ACT_F16 : ACT_F32;
-  auto G = [&](const GemmParams& p, int op, bool split) {
-    return bf ? gemm_mfma(p, op, split, s) : gemm_f32(p, s);
+  auto G = [&](const GemmParams& p, int op) {
+    return bf ? gemm_mfma(p, op, s) : gemm_f32(p, s);
   };
 
   ST_TRY(run(b, ST_K_GN_STATS, s, [&] {
@@ -454,7 +466,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
            if (e != hipSuccess) return e;
            GemmParams p = gemm(b->u, C, b->w_in, C, T, C, C, EPI_STORE_F32);
            p.epi.bias = b->b_in; p.epi.out_f32 = b->h; p.epi.ldo = C;
-           return G(p, ACT_F16, false);
+           return G(p, ACT_F16);
          }), "proj_in");
   int stage = 0;
   auto dump = [&]() -> bool { return stop_stage >= 0 && stage == stop_stage; };
@@ -472,7 +484,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
            p.epi.hs.layer_stride = b->ctx_layer_stride;
            p.epi.hs.rows_per_batch = ST_CTX_LEN; p.epi.hs.npad = b->cpad;
            p.epi.hs.heads = b->heads; p.epi.hs.C = C;
-           return G(p, ACT_BF16, false);
+           return G(p, ACT_BF16);
          }), "context K/V projection");
 
   for (int l = 0; l < b->depth; ++l) {
@@ -488,7 +500,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              p.epi.hs.transposed_mask = 4; p.epi.hs.nsplit = 3; p.epi.hs.layer_stride = 0;
              p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
              p.epi.hs.heads = b->heads; p.epi.hs.C = C;
-             return G(p, ACT_F16, false);
+             return G(p, ACT_F16);
            }), "Q/K/V projection");
     ST_TRY(run(b, ST_K_SELF_ATTN, s, [&] {
              AttnParams a{};
@@ -500,7 +512,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
              GemmParams p = gemm(b->o, C, L.wo1, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo1; p.epi.out_f32 = b->h; p.epi.ldo = C;
-             return G(p, ACT_BF16, false);
+             return G(p, ACT_BF16);
            }), "self-attention out-projection");
     ++stage;
     if (dump()) break;
@@ -515,7 +527,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              p.epi.hs.transposed_mask = 0; p.epi.hs.nsplit = 1; p.epi.hs.layer_stride = 0;
              p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
              p.epi.hs.heads = b->heads; p.epi.hs.C = C;
-             return G(p, ACT_F16, false);
+             return G(p, ACT_F16);
            }), "cross-attention Q projection");
     ST_TRY(run(b, ST_K_CROSS_ATTN, s, [&] {
              AttnParams a{};
@@ -530,7 +542,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
              GemmParams p = gemm(b->o, C, L.wo2, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo2; p.epi.out_f32 = b->h; p.epi.ldo = C;
-             return G(p, ACT_BF16, false);
+             return G(p, ACT_BF16);
            }), "cross-attention out-projection");
     ++stage;
     if (dump()) break;
@@ -542,7 +554,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              if (bf) {
                GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_GEGLU);
                p.epi.bias = L.b1; p.epi.out_act = b->f; p.epi.F = F;
-               return gemm_mfma(p, ACT_F16, false, s);
+               return gemm_mfma(p, ACT_F16, s);
              }
              GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_STORE_F32);
              p.epi.bias = L.b1; p.epi.out_f32 = b->z; p.epi.ldo = 2 * F;
@@ -553,7 +565,9 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_FF2, s, [&] {
              GemmParams p = gemm(b->f, F, L.w2, F, T, C, F, EPI_RESID_F32);
              p.epi.bias = L.b2; p.epi.out_f32 = b->h; p.epi.ldo = C;
-             return G(p, ACT_F16, false);
+             // the last layer also leaves h as two bf16 terms for proj_out
+             if (bf && l + 1 == b->depth && stop_stage < 0) p.epi.out_act = b->hsplit;
+             return G(p, ACT_F16);
            }), "feed-forward 2");
     ++stage;
     if (dump()) break;
@@ -567,10 +581,13 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   ST_TRY(run(b, ST_K_PROJ_OUT, s, [&] {
            // y^T orientation: rows = channels, columns = tokens, so the NCHW
            // store is contiguous along tokens.
-           GemmParams p = gemm(b->w_out, C, b->h, C, C, T, C, EPI_NCHW);
+           // bf16: y^T = [W_out | W_out] [h_hi | h_lo]^T, K = 2C, so that
+           // the fp32 residual stream enters with ~16 significant bits.
+           GemmParams p = bf ? gemm(b->w_out, 2 * C, b->hsplit, 2 * C, C, T, 2 * C, EPI_NCHW)
+                             : gemm(b->w_out, C, b->h, C, C, T, C, EPI_NCHW);
            p.epi.bias = b->b_out; p.epi.out_act = y; p.epi.resid_act = x;
            p.epi.ntok = N; p.epi.ldo = C;
-           return G(p, ACT_BF16, true);
+           return G(p, ACT_BF16);
          }), "proj_out");
   return ST_OK;
 }

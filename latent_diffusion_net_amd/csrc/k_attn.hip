@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   // instead of being hoisted out of the loop into 32 live masks.
   auto mask_tile = [&](int t, floatx16 (&sc)[QB][2]) {
     int kvalid = p.Nk - t * KT;
-    asm volatile("" : "+s"(kvalid));
+    asm volatile("" : "+v"(kvalid));
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll

@@ -4,18 +4,18 @@
 // 16-bit operands (bf16 or fp16) on v_mfma_f32_32x32x16 with fp32
 // accumulation.  A 256-thread workgroup owns a 128x128 output tile; each of
 // its four wavefronts owns a 64x64 quarter as 2x2 MFMA blocks of 32x32 (64
-// fp32 accumulators per lane).  K advances 32 at a time through a ring of
-// four LDS stages filled by global_load_lds_dwordx4 (no staging registers),
-// so three stages are in flight while one is consumed, with one barrier per
-// stage.  Each stage buffer is its own LDS object: the compiler can then
-// tell a DMA into one stage from reads of another and does not wait on it.
-// LDS rows are 64 bytes (32 elements, four 16-byte chunks); chunk c of row r
-// is stored at c ^ ((r >> 2) & 3), which spreads the 16 rows of one
-// 16-lane read phase over all 16 bank groups of gfx950's 64-bank LDS.  Rows
-// beyond M or N are clamped on load and masked on store.
+// fp32 accumulators per lane).  K advances 64 at a time through a ring of
+// LDS stages filled by global_load_lds_dwordx4 (no staging registers), with
+// one barrier per stage.  Each stage buffer is its own LDS object: the
+// compiler can then tell a DMA into one stage from reads of another and does
+// not wait on it.  LDS rows are 128 bytes (64 elements, eight 16-byte
+// chunks); chunk c of row r is stored at c ^ ((r >> 1) & 7), which spreads
+// the 16 rows of one 16-lane read phase over all 16 bank groups of gfx950's
+// 64-bank LDS.  Rows beyond M or N are clamped on load and masked on store.
 //
-// B given as fp32 (the residual stream entering proj_out) goes through a
-// register-staged variant that splits each value into two bf16 terms.
+// The residual epilogue can also leave the new fp32 value as two bf16 terms
+// (hi, lo) so that proj_out can take the residual stream at ~16 significant
+// bits through the same bf16 kernel with K doubled.
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
@@ -27,35 +27,28 @@ namespace stb {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128;
 constexpr int kThreads = 256;
 
-// 128-byte rows (64 elements): chunk c of row r at c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
+// Output tile of this workgroup (1-D grid of mt * nt workgroups).
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
+// each XCD is given a contiguous run of logical tiles; logical tiles walk
+// groups of up to 4 M-tiles, M fastest, then N.  The A rows of a group and
+// the few B tiles its resident workgroups share then stay in one L2 instead
+// of every XCD streaming all of B.
+__device__ __forceinline__ void tile_coords(int mt, int nt, int& tm, int& tn) {
+  constexpr int G = 4;
+  const int total = mt * nt;
+  int b = blockIdx.x;
+  if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
+  const int group = b / (G * nt);
+  const int first = group * G;
+  const int gm = min(G, mt - first);
+  const int r = b - group * G * nt;
+  tn = r / gm;
+  tm = first + (r - tn * gm);
 }
 
-// One 8-element chunk of B.  SPLIT: B is fp32 and the chunk holds its bf16
-// high part (lo == false) or the bf16 rounding of the remainder (lo == true).
-template <bool SPLIT>
-__device__ __forceinline__ uint4 load_b_chunk(const void* B, long long ldb,
-                                              long long row, int k, bool lo) {
-  if constexpr (SPLIT) {
-    const float4* p = reinterpret_cast<const float4*>(
-        static_cast<const float*>(B) + row * ldb + k);
-    const float4 x0 = p[0], x1 = p[1];
-    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    if (lo) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] -= bf2f(f2bf(v[i]));
-    }
-    return make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]),
-                      pack2bf(v[4], v[5]), pack2bf(v[6], v[7]));
-  } else {
-    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(B) +
-                                           row * ldb + k);
-  }
-}
 
 // Head-split store of four consecutive rows (tokens) of one column.  For a
 // V^T destination the four values are contiguous and go out as one 8-byte
@@ -151,6 +144,16 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         v.x += hin[it].x; v.y += hin[it].y; v.z += hin[it].z; v.w += hin[it].w;
       }
       *reinterpret_cast<float4*>(p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = v;
+      if constexpr (EPI == EPI_RESID_F32) {
+        if (p.epi.out_act) {
+          // h = hi + lo in bf16: hi in columns [0, ldo), lo in [ldo, 2 ldo)
+          const uint32_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+          bf16_t* hs = static_cast<bf16_t*>(p.epi.out_act) + static_cast<long long>(row) * 2 * p.epi.ldo + C0 + lc;
+          *reinterpret_cast<uint2*>(hs) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          *reinterpret_cast<uint2*>(hs + p.epi.ldo) =
+              make_uint2(pack2bf(v.x - bf2f(h0), v.y - bf2f(h1)), pack2bf(v.z - bf2f(h2), v.w - bf2f(h3)));
+        }
+      }
     }
   } else if constexpr (EPI == EPI_GEGLU) {
     // columns 0..31 are values, 32..63 the matching gates; output
@@ -291,88 +294,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
   }
 }
 
-template <int EPI, typename OpT, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const uint16_t* A = static_cast<const uint16_t*>(p.A);
-  const int M = p.M, N = p.N;
-  const int nkh = p.K / BK;                 // K steps over the real K
-  const int nk = SPLIT ? 2 * nkh : nkh;     // SPLIT: hi pass then lo pass
-
-  // Each thread stages 4 chunks of 8 elements of A and of B per K step.
-  uint4 ra[4], rb[4];
-  auto load_tile = [&](int kt) {
-    const bool lo = SPLIT && kt >= nkh;
-    const int k0 = (lo ? kt - nkh : kt) * BK;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = tid + kThreads * r;
-      const int row = q >> 3, c = q & 7;
-      const long long gm = min(m0 + row, M - 1);
-      const long long gn = min(n0 + row, N - 1);
-      ra[r] = *reinterpret_cast<const uint4*>(A + gm * p.lda + k0 + c * 8);
-      rb[r] = load_b_chunk<SPLIT>(p.B, p.ldb, gn, k0 + c * 8, lo);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = tid + kThreads * r;
-      const int row = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][lds_off(row, c)]) = ra[r];
-      *reinterpret_cast<uint4*>(&sB[buf][lds_off(row, c)]) = rb[r];
-    }
-  };
-
-  floatx16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  const int l32 = lane & 31, lhi = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int chunk = 2 * s + lhi;
-      uint4 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const uint4*>(&sA[buf][lds_off(wm * 64 + i * 32 + l32, chunk)]);
-        b[i] = *reinterpret_cast<const uint4*>(&sB[buf][lds_off(wn * 64 + i * 32 + l32, chunk)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j], OpT{});
-    }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // every wavefront is done reading the stage buffers before they hold
-  // the epilogue tiles
-  stage_barrier();
-  float* stage = reinterpret_cast<float*>(wave == 0 ? &sA[0][0] : wave == 1 ? &sA[1][0]
-                                          : wave == 2 ? &sB[0][0] : &sB[1][0]);
-  epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
-}
-
 // ------------------------------------------------------- DMA-ring GEMM
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -406,8 +327,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  int tm, tn;
+  tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int M = p.M, N = p.N;
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* Bm = static_cast<const uint16_t*>(p.B);
@@ -555,16 +478,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 #endif
 constexpr int kBKT = ST_GEMM_BKT, kNST = ST_GEMM_NST;
 
-hipError_t gemm_mfma(const GemmParams& p, int op, bool b_split_f32,
-                     hipStream_t s) {
+hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (p.K % BK) return hipErrorInvalidValue;
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
-  if (b_split_f32) {
-    if (op != ACT_BF16 || p.epi.kind != EPI_NCHW) return hipErrorInvalidValue;
-    gemm_mfma_kernel<EPI_NCHW, bf16_t, true><<<grid, kThreads, 0, s>>>(p);
-    return hipGetLastError();
-  }
+  if (p.K % kBKT) return hipErrorInvalidValue;
+  const dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
 #define ST_GEMM_CASE(E)                                                     \
   case E:                                                                   \
     if (op == ACT_F16) gemm_dma_kernel<E, f16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p); \

@@ -38,7 +38,9 @@ struct EpiParams {
   const float* bias;      // by column; by row for EPI_NCHW; may be NULL
   float* out_f32;         // EPI_STORE_F32 / EPI_RESID_F32
   int ldo;
-  void* out_act;          // EPI_GEGLU: [M][F]; EPI_NCHW: y [B][M][ntok]
+  void* out_act;          // EPI_GEGLU: [M][F]; EPI_NCHW: y [B][M][ntok];
+                          // EPI_RESID_F32 (optional): the new value as bf16
+                          // hi + lo, [M][2 ldo] (hi in [0, ldo), lo after)
   const void* resid_act;  // EPI_NCHW: x [B][M][ntok]
   int F;                  // EPI_GEGLU: value width
   int ntok;               // EPI_NCHW: tokens per sample
@@ -56,12 +58,9 @@ struct GemmParams {
 };
 
 // MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
-// ACT_F16 and gives the type of A and B.  With `b_split_f32`, B is fp32 in
-// memory and enters as two bf16 terms, hi = bf16(b) and lo = bf16(b - hi),
-// so that the product keeps about 16 significant bits of B (op must be
-// ACT_BF16).  Requires K % 64 == 0 and 16-byte aligned rows; any M, N.
-hipError_t gemm_mfma(const GemmParams& p, int op, bool b_split_f32,
-                     hipStream_t s);
+// ACT_F16 and gives the type of A and B.  Requires K % 64 == 0 and 16-byte
+// aligned rows; any M, N.
+hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s);
 // fp32 everything (debug path).  Requires K % 16 == 0.
 hipError_t gemm_f32(const GemmParams& p, hipStream_t s);
 
