@@ -107,6 +107,8 @@ struct st_block {
   float* z;  // fp32 path: FF1 output before GEGLU
   void *kc, *vct;
   long long ctx_layer_stride;
+  int ctx_ksplit;   // bf16 path: K slices of the context K/V GEMM (1 = none)
+  float* ctx_ws;    // [ctx_ksplit][B*77][depth*2C] fp32 partial products
 
   hipStream_t last_stream;
   unsigned timing_mask;
@@ -366,6 +368,20 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->f = cr.alloc(T * F * es, "GEGLU output");
   b->z = b->bf16 ? nullptr : static_cast<float*>(cr.alloc(T * 2LL * F * sizeof(float), "FF1 output"));
   b->ctx_layer_stride = static_cast<long long>(B) * heads * b->cpad * 64;
+  // The context K/V GEMM has only B*77 rows: with few output tiles it
+  // splits K so that enough workgroups stream the weights.
+  {
+    const int ctx_rows = B * ST_CTX_LEN;
+    const long long tiles = ((ctx_rows + 127) / 128) * ((kvrows + 127) / 128);
+    b->ctx_ksplit = 1;
+    if (b->bf16 && tiles < 128)
+      for (int sp = 8; sp > 1; sp /= 2)
+        if (D_ctx % (sp * 64) == 0) { b->ctx_ksplit = sp; break; }
+    b->ctx_ws = b->ctx_ksplit > 1
+                    ? static_cast<float*>(cr.alloc(sizeof(float) * b->ctx_ksplit * ctx_rows * kvrows,
+                                                   "context K/V partial products"))
+                    : nullptr;
+  }
   b->kc = cr.alloc(b->ctx_layer_stride * depth * es, "context K");
   b->vct = cr.alloc(b->ctx_layer_stride * depth * es, "context V^T");
   // Padding rows of the per-head buffers are read by the attention kernels
@@ -484,6 +500,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
            p.epi.hs.layer_stride = b->ctx_layer_stride;
            p.epi.hs.rows_per_batch = ST_CTX_LEN; p.epi.hs.npad = b->cpad;
            p.epi.hs.heads = b->heads; p.epi.hs.C = C;
+           p.ksplit = b->ctx_ksplit; p.ws = b->ctx_ws;
            return G(p, ACT_BF16);
          }), "context K/V projection");
 

@@ -36,10 +36,10 @@ constexpr int kThreads = 256;
 // groups of up to 4 M-tiles, M fastest, then N.  The A rows of a group and
 // the few B tiles its resident workgroups share then stay in one L2 instead
 // of every XCD streaming all of B.
-__device__ __forceinline__ void tile_coords(int mt, int nt, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int mt, int nt, int bid, int& tm, int& tn) {
   constexpr int G = 4;
   const int total = mt * nt;
-  int b = blockIdx.x;
+  int b = bid;
   if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
   const int group = b / (G * nt);
   const int first = group * G;
@@ -327,8 +327,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // split-K: workgroup blockIdx.x takes tile blockIdx.x % tiles and K slice
+  // blockIdx.x / tiles (always 0 without split)
+  const int mt = (p.M + BM - 1) / BM, nt = (p.N + BN - 1) / BN;
+  const int kz = blockIdx.x / (mt * nt);
+  const int kslice = p.K / (p.ksplit > 1 ? p.ksplit : 1);
   int tm, tn;
-  tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  tile_coords(mt, nt, blockIdx.x - kz * mt * nt, tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int M = p.M, N = p.N;
@@ -344,8 +349,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
     const int row = RPB * (wave * DPW + j2) + lane / CPR;
     const int pc = lane % CPR;
     const int cl = (BKT == 64) ? (pc ^ ((row >> 1) & 7)) : (pc ^ ((row >> 2) & 3));
-    aoff[j2] = static_cast<long long>(min(m0 + row, M - 1)) * p.lda + cl * 8;
-    boff[j2] = static_cast<long long>(min(n0 + row, N - 1)) * p.ldb + cl * 8;
+    aoff[j2] = static_cast<long long>(min(m0 + row, M - 1)) * p.lda + static_cast<long long>(kz) * kslice + cl * 8;
+    boff[j2] = static_cast<long long>(min(n0 + row, N - 1)) * p.ldb + static_cast<long long>(kz) * kslice + cl * 8;
   }
   auto issue = [&](int k, uint16_t* sa, uint16_t* sb) {
 #pragma unroll
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
   // Iteration k: stage k must have landed (later stages may still be in
   // flight), every wavefront must be past iteration k-1 (whose buffer is
   // refilled now with stage k + NST - 1), then stage k is consumed.
-  const int nk = p.K / BKT;
+  const int nk = kslice / BKT;
   constexpr int PER = 2 * DPW;  // DMA instructions per stage per wavefront
   issue(0, sA0, sB0);
   if (nk > 1 && NST > 2) issue(1, sA1, sB1);
@@ -420,7 +425,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
   // the epilogue tiles
   stage_barrier();
   float* stage = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1);
-  epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
+  if (p.ksplit > 1) {
+    // this slice's product, plain fp32, into ws[kz]
+    GemmParams q = p;
+    q.epi.kind = EPI_STORE_F32;
+    q.epi.bias = nullptr;
+    q.epi.out_f32 = p.ws + static_cast<long long>(kz) * M * N;
+    q.epi.ldo = N;
+    epilogue_lds<EPI_STORE_F32>(q, acc, m0, n0, wm, wn, lane, stage);
+  } else {
+    epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
+  }
+}
+
+// Second pass of split-K: the slices added in order (deterministic), then
+// the epilogue of one element.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
+  const long long mn = static_cast<long long>(p.M) * p.N;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= mn) return;
+  float acc = 0.f;
+  for (int z = 0; z < p.ksplit; ++z) acc += p.ws[z * mn + idx];
+  const int row = static_cast<int>(idx / p.N);
+  epi_store<EPI, bf16_t>(p.epi, row, static_cast<int>(idx - static_cast<long long>(row) * p.N), acc);
 }
 
 // ---------------------------------------------------------------- fp32 GEMM
@@ -481,7 +509,22 @@ constexpr int kBKT = ST_GEMM_BKT, kNST = ST_GEMM_NST;
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.K % kBKT) return hipErrorInvalidValue;
-  const dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
+  const int split = p.ksplit > 1 ? p.ksplit : 1;
+  if (split > 1 && (!p.ws || p.K % (split * kBKT) || op != ACT_BF16 ||
+                    (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32)))
+    return hipErrorInvalidValue;
+  const dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM) * split);
+  if (split > 1) {
+    // the slices (the kernel switches to the plain fp32 store), then the sum
+    gemm_dma_kernel<EPI_STORE_F32, bf16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long mn = static_cast<long long>(p.M) * p.N;
+    const unsigned blocks = static_cast<unsigned>((mn + 255) / 256);
+    if (p.epi.kind == EPI_HEADS) splitk_reduce_kernel<EPI_HEADS><<<blocks, 256, 0, s>>>(p);
+    else splitk_reduce_kernel<EPI_STORE_F32><<<blocks, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
 #define ST_GEMM_CASE(E)                                                     \
   case E:                                                                   \
     if (op == ACT_F16) gemm_dma_kernel<E, f16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p); \

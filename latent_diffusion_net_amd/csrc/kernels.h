@@ -55,6 +55,11 @@ struct GemmParams {
   long long ldb;
   int M, N, K;
   EpiParams epi;
+  // Split-K (gemm_mfma only): with ksplit > 1, K is cut into ksplit equal
+  // slices whose fp32 products land in ws[ksplit][M][N]; a second pass adds
+  // the slices in order and applies the epilogue element by element.
+  int ksplit;
+  float* ws;
 };
 
 // MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
