@@ -107,6 +107,8 @@ struct st_block {
   float* z;  // fp32 path: FF1 output before GEGLU
   void *kc, *vct;
   long long ctx_layer_stride;
+  int attn_n_full, attn_nsplit;  // bf16 self-attention load-balance plan
+  float* attn_part;
   int ctx_ksplit;   // bf16 path: K slices of the context K/V GEMM (1 = none)
   float* ctx_ws;    // [ctx_ksplit][B*77][depth*2C] fp32 partial products
 
@@ -382,6 +384,26 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
                                                    "context K/V partial products"))
                     : nullptr;
   }
+  // Self-attention load balance: with more query tiles than fit a whole
+  // number per CU, the remainder is split over keys (ST_ATTN_CUS overrides
+  // the CU count the plan assumes; it changes only the work split).
+  b->attn_n_full = 0;
+  b->attn_nsplit = 1;
+  b->attn_part = nullptr;
+  if (b->bf16 && cr.ok()) {
+    int cus = 0;
+    cr.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    if (const char* e = std::getenv("ST_ATTN_CUS")) cus = std::atoi(e);
+    attention_bf16_plan(B, heads, b->N, b->N, cus, b->attn_n_full, b->attn_nsplit);
+    if (b->attn_nsplit > 1) {
+      const long long split_tiles =
+          static_cast<long long>(B) * heads * ((b->N + attention_bf16_q_tile() - 1) / attention_bf16_q_tile()) -
+          b->attn_n_full;
+      b->attn_part = static_cast<float*>(cr.alloc(
+          sizeof(float) * split_tiles * b->attn_nsplit * attention_bf16_part_floats(),
+          "self-attention partial results"));
+    }
+  }
   b->kc = cr.alloc(b->ctx_layer_stride * depth * es, "context K");
   b->vct = cr.alloc(b->ctx_layer_stride * depth * es, "context V^T");
   // Padding rows of the per-head buffers are read by the attention kernels
@@ -524,6 +546,8 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              a.q = b->q; a.k = b->k; a.vt = b->vt; a.o = b->o;
              a.B = B; a.heads = b->heads; a.C = C; a.Nq = N; a.Nk = N;
              a.q_pad = b->npad; a.kv_pad = b->npad;
+             a.n_full = b->attn_n_full; a.nsplit = b->attn_nsplit;
+             a.part = b->attn_part;
              return bf ? attention_bf16(a, s) : attention_f32(a, s);
            }), "self-attention");
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {

@@ -85,15 +85,27 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
-  // consecutive logical tiles (the same sample and head, hence the same K
-  // and V) are given to one XCD and share its L2.
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // Workgroups [0, n_full) take whole query tiles, the rest one key range
+  // (piece) of a split tile.  Within each group, XCD-aware order:
+  // workgroups are dealt round-robin to the 8 XCDs, so consecutive logical
+  // tiles (the same sample and head, hence the same K and V) are given to
+  // one XCD and share its L2.
+  const int ntiles_all = (p.Nk + KT - 1) / KT;
+  const int nsplit = p.nsplit > 1 ? p.nsplit : 1;
+  auto xcd_order = [](int h, int n) { return (n & 7) ? h : (h & 7) * (n >> 3) + (h >> 3); };
+  int tile, piece = -1, kt0 = 0, kt1 = ntiles_all;
+  if (nsplit == 1 || static_cast<int>(blockIdx.x) < p.n_full) {
+    tile = xcd_order(blockIdx.x, nsplit == 1 ? gridDim.x : p.n_full);
+  } else {
+    const int r = xcd_order(blockIdx.x - p.n_full, gridDim.x - p.n_full);
+    tile = p.n_full + r / nsplit;
+    piece = r - (r / nsplit) * nsplit;
+    kt0 = piece * ntiles_all / nsplit;
+    kt1 = (piece + 1) * ntiles_all / nsplit;
+  }
   const int qtiles = (p.Nq + QT - 1) / QT;
-  const int bh = bid / qtiles;
-  const int qt = bid - bh * qtiles;
+  const int bh = tile / qtiles;
+  const int qt = tile - bh * qtiles;
   const int b = bh / p.heads;
   const int head = bh - b * p.heads;
   const int q0 = qt * QT + wave * QW;
@@ -163,7 +175,6 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   auto lds_operand = [&](const uint16_t* buf, int half, int s4) -> uint4 {
     return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(buf) + half * 4096 + lo[s4]);
   };
-  const int ntiles = (p.Nk + KT - 1) / KT;
 
   // S^T = K Q^T for one tile; sc[qb][kb] entry r: tile row
   // kb*32 + 8*(r/4) + 4*lhi + r%4 (key perm of it), query q0 + 32qb + l32.
@@ -275,23 +286,26 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   // of K_{t+3} and V_{t+2}, so that every tile has two iterations to arrive.
   // The exact max of tile 0 is taken in the prologue and a ragged last tile
   // is masked as soon as its scores exist.
-  const int ragged_last = (p.Nk % KT) ? ntiles - 1 : -1;
+  // Tiles kt0 .. kt1-1 (all of them unless this workgroup is one piece of a
+  // split tile); t below counts from kt0.
+  const int ragged_last = (p.Nk % KT) ? ntiles_all - 1 : -1;
+  const int ntiles = kt1 - kt0;
   floatx16 sc[QB][2];  // S_t
-  issue_k(0, sK0);
-  issue_v(0, sV0);
-  if (ntiles > 1) { issue_k(1, sK1); issue_v(1, sV1); }
-  if (ntiles > 2) issue_k(2, sK2);
+  issue_k(kt0, sK0);
+  issue_v(kt0, sV0);
+  if (ntiles > 1) { issue_k(kt0 + 1, sK1); issue_v(kt0 + 1, sV1); }
+  if (ntiles > 2) issue_k(kt0 + 2, sK2);
   wait_vmcnt_lds<0>();
   stage_barrier();
   qk(sK0, sc);
-  if (ragged_last == 0) mask_tile(0, sc);
+  if (ragged_last == kt0) mask_tile(kt0, sc);
   exact_max(sc);
   stage_barrier();  // every wavefront is done with K_0 before K_3 replaces it
 
   constexpr int kIssued = 2 * BPW;  // DMA instructions per wavefront per iteration
   auto iter = [&](int t, const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
-    if (t + 3 < ntiles) issue_k(t + 3, kw);
-    if (t + 2 < ntiles) issue_v(t + 2, vw);
+    if (t + 3 < ntiles) issue_k(kt0 + t + 3, kw);
+    if (t + 2 < ntiles) issue_v(kt0 + t + 2, vw);
     uint4 pb[QB][4];
     float ps[QB];
     if (__any(exponentiate(sc, pb, ps))) {  // rare
@@ -303,7 +317,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     // S_{t+1} (unused past the last tile: its LDS buffer then holds stale,
     // finite data)
     qk(kn, sc);
-    if (t + 1 == ragged_last) mask_tile(t + 1, sc);
+    if (kt0 + t + 1 == ragged_last) mask_tile(kt0 + t + 1, sc);
     pv(vc, pb);
     // K_{t+2} and V_{t+1} have landed (loads complete in order, so at most
     // this iteration's own DMA is still in flight)
@@ -322,11 +336,38 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   if (t < ntiles) iter(t, sK1, sV0, sK0, sV2);
   if (t + 1 < ntiles) iter(t + 1, sK2, sV1, sK1, sV0);
 
-  // Row sums over both lane halves, normalise, store O[token][head*64 + d].
+  // Row sums over both lane halves.  Lane l holds O^T entries of query
+  // q0 + 32qb + l32, dims db*32 + 8g + 4*lhi + 0..3 (g = r / 4).
+  float l_tot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = lsum[qb] + __shfl_xor(lsum[qb], 32, 64);
+
+  if (piece >= 0) {
+    // One piece of a split tile: store the partial result (unnormalised O,
+    // reference max, row sum) for the merge pass.
+    constexpr int PF = QT * 66;  // per piece: O [QT][64], max [QT], sum [QT]
+    float* mine = p.part + (static_cast<long long>(tile - p.n_full) * nsplit + piece) * PF;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wave * QW + qb * 32 + l32;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(mine + row * 64 + db * 32 + 8 * g + 4 * lhi) =
+              make_float4(o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]);
+      if (lhi == 0) {
+        mine[QT * 64 + row] = mref[qb];
+        mine[QT * 65 + row] = l_tot[qb];
+      }
+    }
+    return;  // attn_merge_kernel combines the pieces
+  }
+
+  // Whole tile: normalise, store O[token][head*64 + d].
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = lsum[qb] + __shfl_xor(lsum[qb], 32, 64);
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / l_tot[qb];
     const int qrow = q0 + qb * 32 + l32;
     if (qrow < p.Nq) {
       uint16_t* orow = static_cast<uint16_t*>(p.o) +
@@ -342,6 +383,55 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
         }
     }
   }
+}
+
+// Second pass of the key split: for each split query tile, the pieces'
+// partial results are merged in piece order (bitwise reproducible):
+// O = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^((m_i - max_i m_i) c).
+// Two threads per query row, 32 dims each.
+template <int QT>
+__global__ __launch_bounds__(2 * QT) void attn_merge_kernel(AttnParams p) {
+  constexpr int PF = QT * 66;
+  const float c = 0.125f * kLog2e;
+  const int j = blockIdx.x;  // split tile index
+  const int tile = p.n_full + j;
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int qtiles = (p.Nq + QT - 1) / QT;
+  const int bh = tile / qtiles;
+  const int qrow = (tile - bh * qtiles) * QT + row;
+  if (qrow >= p.Nq) return;
+  const int b = bh / p.heads, head = bh - b * p.heads;
+  const float* tp = p.part + static_cast<long long>(j) * p.nsplit * PF;
+  float mmax = -INFINITY;
+  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, tp[i * PF + QT * 64 + row]);
+  float acc[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) acc[d] = 0.f;
+  float den = 0.f;
+  for (int i = 0; i < p.nsplit; ++i) {
+    const float* pi = tp + i * PF;
+    const float w = __builtin_amdgcn_exp2f((pi[QT * 64 + row] - mmax) * c);
+    den += pi[QT * 65 + row] * w;
+    const float4* src = reinterpret_cast<const float4*>(pi + row * 64 + half * 32);
+#pragma unroll
+    for (int d4 = 0; d4 < 8; ++d4) {
+      const float4 v = src[d4];
+      acc[4 * d4] += v.x * w;
+      acc[4 * d4 + 1] += v.y * w;
+      acc[4 * d4 + 2] += v.z * w;
+      acc[4 * d4 + 3] += v.w * w;
+    }
+  }
+  const float inv = 1.0f / den;
+  uint16_t* orow = static_cast<uint16_t*>(p.o) +
+                   (static_cast<long long>(b) * p.Nq + qrow) * p.C + head * 64 + half * 32;
+#pragma unroll
+  for (int d8 = 0; d8 < 4; ++d8)
+    *reinterpret_cast<uint4*>(orow + 8 * d8) =
+        make_uint4(pack2bf(acc[8 * d8] * inv, acc[8 * d8 + 1] * inv),
+                   pack2bf(acc[8 * d8 + 2] * inv, acc[8 * d8 + 3] * inv),
+                   pack2bf(acc[8 * d8 + 4] * inv, acc[8 * d8 + 5] * inv),
+                   pack2bf(acc[8 * d8 + 6] * inv, acc[8 * d8 + 7] * inv));
 }
 
 #ifndef ST_ATTN_QB
@@ -406,15 +496,47 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(AttnParams p) {
 
 int attention_bf16_q_tile() { return kQT; }
 int attention_bf16_kv_tile() { return KT; }
+int attention_bf16_part_floats() { return kQT * 66; }
+
+void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full, int& nsplit) {
+  const int tiles = B * heads * ((Nq + kQT - 1) / kQT);
+  const int ktiles = (Nk + KT - 1) / KT;
+  n_full = tiles;
+  nsplit = 1;
+  if (cus <= 0) return;
+  const int full = (tiles / cus) * cus;  // a whole number of tiles per CU
+  const int rest = tiles - full;
+  if (rest == 0) return;
+  // about one piece per CU, each of at least 16 key tiles: shorter pieces
+  // (and the merge pass) cost more than the balance gains (measured: 23 ->
+  // 26-31 us with 4-tile pieces at 1024 keys; 108 -> 105 us with 32-tile
+  // pieces at 4096 keys)
+  int sp = (cus + rest / 2) / rest;
+  sp = sp < 8 ? sp : 8;
+  while (sp > 1 && ktiles / sp < 16) --sp;
+  if (sp <= 1) return;
+  n_full = full;
+  nsplit = sp;
+}
 
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
   const int qtiles = (p.Nq + kQT - 1) / kQT;
+  const int tiles = p.B * p.heads * qtiles;
   if (p.q_pad < qtiles * kQT || p.kv_pad < ((p.Nk + KT - 1) / KT) * KT)
     return hipErrorInvalidValue;  // padded buffers must cover every tile
+  int grid = tiles;
+  if (p.nsplit > 1) {
+    if (!p.part || p.n_full < 0 || p.n_full >= tiles || (p.Nk + KT - 1) / KT < p.nsplit)
+      return hipErrorInvalidValue;
+    grid = p.n_full + (tiles - p.n_full) * p.nsplit;
+  }
   if (p.Nk == kCtxLen)
-    attn_bf16_kernel<1, kQB, kNW><<<p.B * p.heads * qtiles, 64 * kNW, 0, s>>>(p);
+    attn_bf16_kernel<1, kQB, kNW><<<grid, 64 * kNW, 0, s>>>(p);
   else
-    attn_bf16_kernel<0, kQB, kNW><<<p.B * p.heads * qtiles, 64 * kNW, 0, s>>>(p);
+    attn_bf16_kernel<0, kQB, kNW><<<grid, 64 * kNW, 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit <= 1) return e;
+  attn_merge_kernel<kQT><<<tiles - p.n_full, 2 * kQT, 0, s>>>(p);
   return hipGetLastError();
 }
 

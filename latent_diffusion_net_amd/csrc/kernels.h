@@ -80,11 +80,23 @@ struct AttnParams {
   int B, heads, C;
   int Nq, Nk;
   int q_pad, kv_pad;
+  // Load balance of the bf16 kernel (attention_bf16_plan): the first n_full
+  // query tiles, in (b, head, tile) order, are computed whole; every later
+  // tile is split over its key tiles into nsplit pieces whose partial
+  // results (unnormalised O, running max and row sum) go to `part`, and a
+  // second kernel merges them in piece order.  nsplit <= 1: no split.
+  int n_full, nsplit;
+  float* part;        // [tiles - n_full][nsplit][attention_bf16_part_floats()]
 };
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s);
 hipError_t attention_f32(const AttnParams& p, hipStream_t s);
 int attention_bf16_q_tile();   // query rows per workgroup of the bf16 kernel
 int attention_bf16_kv_tile();  // key rows per LDS tile of the bf16 kernel
+int attention_bf16_part_floats();  // partial-result floats per piece
+// Split plan for B*heads*ceil(Nq/q_tile) query tiles over `cus` compute
+// units: whole tiles fill a whole number per CU, the rest are split so that
+// each CU also gets about one piece.  Sets n_full and nsplit.
+void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full, int& nsplit);
 
 // Norms and helpers.  `bf16` flags say whether activations are bf16 (else fp32).
 hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,

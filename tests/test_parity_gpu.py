@@ -211,3 +211,38 @@ def test_forward_rejects_aliasing_on_device():
         blk.forward_stage(x, ctx, 99)
     torch.cuda.synchronize()
     blk.close()
+
+
+@pytest.mark.parametrize("cus,spec", [
+    # 32 query tiles over 12 CUs: 24 whole, 8 split in 2 over 64 key tiles
+    (12, dict(name="split2", B=1, C=64, H=64, W=64, heads=1, D_ctx=64, depth=1)),
+    # ragged keys (3969 = 62 tiles of 64 + 1): 31 whole, 1 split in 3 pieces,
+    # the last of which holds the ragged tile
+    (31, dict(name="split3_ragged", B=1, C=64, H=63, W=63, heads=1, D_ctx=64, depth=1)),
+    # every tile split in 2, two layers
+    (64, dict(name="split2_all", B=1, C=64, H=64, W=64, heads=1, D_ctx=64, depth=2)),
+], ids=lambda v: v if isinstance(v, int) else v["name"])
+def test_self_attention_split_over_keys(cus, spec, monkeypatch):
+    """Self-attention with query tiles split over key ranges (the load
+    balance used when tiles do not fill the CUs evenly), forced at a small
+    size by planning for fewer CUs: parity with the oracle, and repeated
+    forwards bitwise equal (the pieces are merged in a fixed order)."""
+    import torch
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    monkeypatch.setenv("ST_ATTN_CUS", str(cus))
+    spec = dict(spec)
+    cfg = synth.BlockConfig(spec.pop("name"), dtype="bf16", **spec)
+    inp = synth.make_inputs(cfg, 21, bias_std=0.05, norm_std=0.2)
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    _say(f"[gpu] {cfg.name}: planned for {cus} CUs")
+    p = params_to_device(inp["params"], "bf16")
+    x = array_to_device(inp["x"], "bf16")
+    ctx = array_to_device(inp["ctx"], "bf16")
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    y1 = blk.forward(x, ctx)
+    y2 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    y = y1.float().cpu().numpy().astype(np.float64)
+    blk.close()
+    check(cfg, inp, y, yo)
