@@ -3,8 +3,8 @@
 // launch schedule of one forward.  Declared in include/st_block.h.
 //
 // Launch schedule of one forward (bf16 storage):
-//   GroupNorm statistics            x                     -> (mean, rstd)[B*32]
-//   GroupNorm apply + to tokens     x                     -> u [T][C] bf16
+//   GroupNorm statistics            x                     -> partial sums [B*32][split]
+//   GroupNorm apply + to tokens     x, partial sums       -> u [T][C] fp16
 //   proj_in GEMM                    u, W_in               -> h [T][C] fp32
 //   context K/V GEMM (all layers)   ctx, [Wk2;Wv2]*depth  -> Kc, Vc^T per layer
 //   per layer:
@@ -98,7 +98,7 @@ struct st_block {
   void* wkv;  // [depth*2C][D]: per layer Wk2 rows then Wv2 rows
   float* bkv;
 
-  float2 *gn_part, *gn_stats;
+  float2* gn_part;
   int gn_max_split;
   void* u;
   float* h;
@@ -358,7 +358,6 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   // Workspace.
   b->gn_max_split = 64;
   b->gn_part = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split, "GroupNorm partials"));
-  b->gn_stats = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS, "GroupNorm statistics"));
   b->u = cr.alloc(T * C * es, "normalised activations");
   b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
   b->hsplit = b->bf16 ? cr.alloc(T * 2LL * C * es, "split residual stream") : nullptr;
@@ -497,10 +496,11 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   };
 
   ST_TRY(run(b, ST_K_GN_STATS, s, [&] {
-           return gn_stats(x, bf, B, C, N, b->gn_part, b->gn_max_split, b->gn_stats, s);
+           return gn_stats(x, bf, B, C, N, b->gn_part, b->gn_max_split, s);
          }), "GroupNorm statistics");
   ST_TRY(run(b, ST_K_PROJ_IN, s, [&] {
-           hipError_t e = gn_apply_tokens(x, bf, b->gn_stats, b->gn_w, b->gn_b, b->u, act, B, C, N, s);
+           hipError_t e = gn_apply_tokens(x, bf, b->gn_part, b->gn_max_split, b->gn_w, b->gn_b,
+                                          b->u, act, B, C, N, s);
            if (e != hipSuccess) return e;
            GemmParams p = gemm(b->u, C, b->w_in, C, T, C, C, EPI_STORE_F32);
            p.epi.bias = b->b_in; p.epi.out_f32 = b->h; p.epi.ldo = C;

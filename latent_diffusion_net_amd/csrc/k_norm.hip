@@ -11,11 +11,11 @@ namespace stb {
 // Stage 1: `split` workgroups per group each reduce a slice to the sum and
 // sum of squares of (x - shift), shift = the group's first element (shifted
 // sums keep the variance free of cancellation for data with a large mean).
-// Stage 2: one thread per group adds the partials in fp64 and writes
+// Stage 2 (in the apply kernel): the partials are added in fp64 into
 // (mean, 1/sqrt(var + 1e-6)), population variance.
 
 constexpr int kGnThreads = 256;
-constexpr int kGnSliceMin = 16384;  // elements per workgroup at least
+constexpr int kGnSliceMin = 4096;  // elements per workgroup at least
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float v[8]);
@@ -85,27 +85,6 @@ __global__ __launch_bounds__(kGnThreads) void gn_partial_kernel(
   }
 }
 
-template <typename T>
-__global__ void gn_finalize_kernel(const T* __restrict__ x,
-                                   long long group_elems, int split, int ngroups,
-                                   const float2* __restrict__ partial,
-                                   float2* __restrict__ stats) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= ngroups) return;
-  double s1 = 0.0, s2 = 0.0;
-  for (int s = 0; s < split; ++s) {
-    float2 p = partial[g * split + s];
-    s1 += p.x; s2 += p.y;
-  }
-  const double n = static_cast<double>(group_elems);
-  const double shift = to_f32<T>(x[static_cast<long long>(g) * group_elems]);
-  const double dm = s1 / n;
-  double var = s2 / n - dm * dm;
-  if (var < 0.0) var = 0.0;
-  stats[g] = make_float2(static_cast<float>(shift + dm),
-                         static_cast<float>(1.0 / sqrt(var + 1e-6)));
-}
-
 int gn_split(int C, int N, int max_split) {
   long long elems = static_cast<long long>(C / kGroups) * N;
   long long s = (elems + kGnSliceMin - 1) / kGnSliceMin;
@@ -115,71 +94,115 @@ int gn_split(int C, int N, int max_split) {
 }
 
 hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,
-                    float2* partial, int max_split, float2* stats,
-                    hipStream_t s) {
+                    float2* partial, int max_split, hipStream_t s) {
   const long long group_elems = static_cast<long long>(C / kGroups) * N;
   const int split = gn_split(C, N, max_split);
-  const int ngroups = B * kGroups;
-  dim3 grid(ngroups, split);
-  if (bf16) {
+  dim3 grid(B * kGroups, split);
+  if (bf16)
     gn_partial_kernel<bf16_t><<<grid, kGnThreads, 0, s>>>(
         static_cast<const bf16_t*>(x), group_elems, split, partial);
-    gn_finalize_kernel<bf16_t><<<(ngroups + 63) / 64, 64, 0, s>>>(
-        static_cast<const bf16_t*>(x), group_elems, split, ngroups, partial, stats);
-  } else {
+  else
     gn_partial_kernel<float><<<grid, kGnThreads, 0, s>>>(
         static_cast<const float*>(x), group_elems, split, partial);
-    gn_finalize_kernel<float><<<(ngroups + 63) / 64, 64, 0, s>>>(
-        static_cast<const float*>(x), group_elems, split, ngroups, partial, stats);
-  }
   return hipGetLastError();
 }
 
-// Apply GroupNorm and transpose NCHW -> tokens [B*N][C] through LDS: a
-// workgroup reads a 64-channel x 64-token tile along tokens (coalesced) and
-// writes it along channels (coalesced).
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float v[8]);
+template <>
+__device__ __forceinline__ void store8<f16_t>(f16_t* p, const float v[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]),
+                                            pack2h(v[4], v[5]), pack2h(v[6], v[7]));
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float v[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Apply GroupNorm and transpose NCHW -> tokens [B*N][C] through LDS.  A
+// workgroup owns 64 channels x 64 tokens of one sample.  Its 64 threads
+// first turn the group partial sums into per-channel (scale, offset) =
+// (rstd * gamma, beta - mean * rstd * gamma), combining the slices in fp64
+// (mean = shift + E[x - shift], population variance); then every thread
+// reads 8 consecutive tokens of one channel (16 bytes of bf16) and writes 8
+// consecutive channels of one token.
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
-    const TI* __restrict__ x, const float2* __restrict__ stats,
+    const TI* __restrict__ x, const float2* __restrict__ partial, int split,
     const float* __restrict__ gamma, const float* __restrict__ beta,
     TO* __restrict__ out, int C, int N) {
-  __shared__ float tile[64][65];
+  __shared__ float2 coef[64];
+  __shared__ float tile[64][64 + 4];  // [channel][token]
   const int n0 = blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
   const int b = blockIdx.z;
   const int cg = C / kGroups;
-  const int tx = threadIdx.x & 63;
-  const int ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int c = c0 + r;
-    const int n = n0 + tx;
-    float v = 0.f;
-    if (n < N) {
-      const float2 st = stats[b * kGroups + c / cg];
-      const float xv = to_f32<TI>(x[(static_cast<long long>(b) * C + c) * N + n]);
-      v = (xv - st.x) * st.y * gamma[c] + beta[c];
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int c = c0 + tid;
+    const int g = b * kGroups + c / cg;
+    double s1 = 0.0, s2 = 0.0;
+    for (int i = 0; i < split; ++i) {
+      const float2 pr = partial[g * split + i];
+      s1 += pr.x;
+      s2 += pr.y;
     }
-    tile[r][tx] = v;
+    const double n = static_cast<double>(cg) * N;
+    const double shift = to_f32<TI>(x[static_cast<long long>(g) * cg * N]);
+    const double dm = s1 / n;
+    double var = s2 / n - dm * dm;
+    if (var < 0.0) var = 0.0;
+    const float rstd = static_cast<float>(1.0 / sqrt(var + 1e-6));
+    const float scale = rstd * gamma[c];
+    coef[tid] = make_float2(scale, beta[c] - static_cast<float>(shift + dm) * scale);
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int n = n0 + r;
-    if (n < N)
-      out[(static_cast<long long>(b) * N + n) * C + c0 + tx] = from_f32<TO>(tile[tx][r]);
+  const bool vec_n = (N & 7) == 0;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = pass * 32 + (tid >> 3);
+    const int nl = 8 * (tid & 7);
+    const int n = n0 + nl;
+    const float2 k = coef[cl];
+    const TI* src = x + (static_cast<long long>(b) * C + c0 + cl) * N + n;
+    float v[8];
+    if (vec_n && n + 7 < N) {
+      load8<TI>(src, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = n + j < N ? to_f32<TI>(src[j]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[cl][nl + j] = v[j] * k.x + k.y;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nl = pass * 32 + (tid >> 3);
+    const int cl = 8 * (tid & 7);
+    const int n = n0 + nl;
+    if (n >= N) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = tile[cl + j][nl];
+    store8<TO>(out + (static_cast<long long>(b) * N + n) * C + c0 + cl, v);
   }
 }
 
-hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* stats,
-                           const float* gamma, const float* beta, void* out,
-                           int out_type, int B, int C, int N, hipStream_t s) {
+hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
+                           int max_split, const float* gamma, const float* beta,
+                           void* out, int out_type, int B, int C, int N,
+                           hipStream_t s) {
+  const int split = gn_split(C, N, max_split);
   dim3 grid((N + 63) / 64, C / 64, B);
   if (bf16 && out_type == ACT_F16)
     gn_apply_tokens_kernel<bf16_t, f16_t><<<grid, 256, 0, s>>>(
-        static_cast<const bf16_t*>(x), stats, gamma, beta,
+        static_cast<const bf16_t*>(x), partial, split, gamma, beta,
         static_cast<f16_t*>(out), C, N);
   else if (!bf16 && out_type == ACT_F32)
     gn_apply_tokens_kernel<float, float><<<grid, 256, 0, s>>>(
-        static_cast<const float*>(x), stats, gamma, beta,
+        static_cast<const float*>(x), partial, split, gamma, beta,
         static_cast<float*>(out), C, N);
   else
     return hipErrorInvalidValue;

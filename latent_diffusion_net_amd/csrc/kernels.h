@@ -99,14 +99,18 @@ int attention_bf16_part_floats();  // partial-result floats per piece
 void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full, int& nsplit);
 
 // Norms and helpers.  `bf16` flags say whether activations are bf16 (else fp32).
+// GroupNorm in two launches: gn_stats writes, per (sample, group), the sums
+// of (x - the group's first element) and of its square over gn_split()
+// slices into partial[B*32][split]; gn_apply_tokens combines them (fp64),
+// normalises, applies gamma/beta and transposes NCHW -> tokens [B*N][C] of
+// type `out_type` (ACT_F32 or ACT_F16).
 hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,
-                    float2* partial, int max_split, float2* stats,
-                    hipStream_t s);
+                    float2* partial, int max_split, hipStream_t s);
 int gn_split(int C, int N, int max_split);
-// out: tokens [B*N][C] of type `out_type` (ACT_F32 or ACT_F16).
-hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* stats,
-                           const float* gamma, const float* beta, void* out,
-                           int out_type, int B, int C, int N, hipStream_t s);
+hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
+                           int max_split, const float* gamma, const float* beta,
+                           void* out, int out_type, int B, int C, int N,
+                           hipStream_t s);
 // u: [T][C] of type `out_type` (ACT_F32, ACT_BF16 or ACT_F16).
 hipError_t layernorm(const float* h, const float* gamma, const float* beta,
                      void* u, int out_type, int T, int C, hipStream_t s);
