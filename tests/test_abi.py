@@ -143,3 +143,19 @@ def _load_fresh(path):
         return binding.load_library(path)
     finally:
         binding._lib = saved
+
+
+def test_create_rejects_shapes_beyond_32bit_offsets():
+    """The kernels index activations with 32-bit element offsets; the
+    largest buffer, the GEGLU output [B*H*W][4C], must stay below 2^31
+    elements.  Checked before any device call."""
+    lib = _lib()
+    bw, _keep = _fake_weights()
+    # 1 x 1024 x 1024 tokens x 4*1280 = 5.4e9 elements
+    st, h = _create(lib, B=1, C=1280, H=1024, W=1024, heads=20, w=bw)
+    assert st == binding.ST_ERR_UNSUPPORTED
+    assert h.value is None
+    assert "2^31" in binding.last_error()
+    # just past the limit: 2^31 elements exactly
+    st, h = _create(lib, B=2, C=64, H=2048, W=2048, heads=1, w=bw)
+    assert st == binding.ST_ERR_UNSUPPORTED and h.value is None
