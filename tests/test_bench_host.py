@@ -1,0 +1,86 @@
+"""Host logic of bench.py: FLOP counts, the HBM-traffic summary of two
+counter passes (scaled by the calibration copy) and the rule that the
+committed traffic figure only applies to the kernel source it was taken on."""
+import csv
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_attention_flops_counts_both_products(bench):
+    from latent_diffusion_net_amd import synth
+    cfg = synth.CONFIGS[3]  # SDXL Down1: B=2, 10 heads, N=4096
+    # QK^T and PV: 2 multiply-adds per (query, key, dim) each
+    assert bench.attention_flops(cfg) == 2 * 2 * cfg.B * cfg.heads * cfg.N * cfg.N * 64
+    assert bench.attention_flops(cfg) == pytest.approx(85.899e9, rel=1e-4)
+
+
+def test_block_flops_sums_every_contraction(bench):
+    from latent_diffusion_net_amd import synth
+    cfg = synth.BlockConfig("t", 1, 64, 4, 4, 1, 128, 2, "bf16")
+    T, C, N, D, B = cfg.T, cfg.C, cfg.N, cfg.D_ctx, cfg.B
+    F = 4 * C
+    gemm = lambda m, n, k: 2.0 * m * n * k
+    per_layer = (gemm(T, 3 * C, C) + gemm(T, C, C)        # QKV, out-proj 1
+                 + gemm(T, C, C) + gemm(T, C, C)          # cross Q, out-proj 2
+                 + gemm(B * 77, 2 * C, D)                 # context K/V
+                 + 4.0 * B * N * 77 * C                   # cross-attention
+                 + gemm(T, 2 * F, C) + gemm(T, C, F)      # FF1, FF2
+                 + bench.attention_flops(cfg))
+    total = gemm(T, C, C) * 2 + cfg.depth * per_layer     # + proj_in, proj_out
+    assert bench.block_flops(cfg) == pytest.approx(total)
+
+
+def _write_counters(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_summarize_pmc_scales_by_the_copy_kernel(bench, tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    attn = "void stb::attn_bf16_kernel<0, 1, 4>(stb::AttnParams)"
+    # fetch counter reads half the copy's bytes (factor 2); two launches
+    _write_counters(f, "FETCH_SIZE", [(attn, 1000.0), (attn, 1200.0),
+                                      ("__amd_rocclr_copyBuffer", copy_kib / 2),
+                                      ("__amd_rocclr_copyBuffer", 3.0),
+                                      ("other_kernel", 99999.0)])
+    _write_counters(w, "WRITE_SIZE", [(attn, 500.0), (attn, 500.0),
+                                      ("__amd_rocclr_copyBuffer", copy_kib)])
+    r = bench.summarize_pmc(str(f), str(w))
+    assert r["attn_launches"] == 2
+    assert r["fetch_scale"] == pytest.approx(2.0)
+    assert r["write_scale"] == pytest.approx(1.0)
+    assert r["fetch_bytes"] == pytest.approx(1100.0 * 1024 * 2.0)
+    assert r["write_bytes"] == pytest.approx(500.0 * 1024)
+    assert r["traffic_bytes_per_launch"] == pytest.approx(1100.0 * 2048 + 500.0 * 1024)
+
+
+def test_traffic_figure_is_tied_to_the_kernel_source(bench, tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel v1\n")
+    prof = tmp_path / "traffic.md"
+    monkeypatch.setattr(bench, "ATTN_SRC", str(src))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(prof))
+    assert bench.measured_traffic() is None          # no summary yet
+    prof.write_text(f"traffic_bytes_per_launch: 123.5\n"
+                    f"kernel source sha256[:16]: {bench.source_hash()}\n")
+    assert bench.measured_traffic() == pytest.approx(123.5)
+    src.write_text("// kernel v2\n")                  # source changed
+    assert bench.measured_traffic() is None
+
