@@ -2,13 +2,16 @@
 // both operands K-contiguous (activations [tokens][in], weights [out][in]).
 //
 // 16-bit operands (bf16 or fp16) on v_mfma_f32_32x32x16 with fp32
-// accumulation.  A 256-thread workgroup owns a 128x128 output tile; each of
-// its four wavefronts owns a 64x64 quarter as 2x2 MFMA blocks of 32x32 (64
-// fp32 accumulators per lane).  K advances 64 at a time through a ring of
-// LDS stages filled by global_load_lds_dwordx4 (no staging registers), with
-// one barrier per stage.  Each stage buffer is its own LDS object: the
-// compiler can then tell a DMA into one stage from reads of another and does
-// not wait on it.  LDS rows are 128 bytes (64 elements, eight 16-byte
+// accumulation.  A workgroup of WM x WN wavefronts owns a tile of
+// (WM*FM*32) x (WN*FN*32) outputs, each wavefront FM x FN MFMA blocks of
+// 32x32: 128x128 tiles of four 64x64 wavefronts (two workgroups per CU), or
+// 256x256 tiles of eight 128x64 wavefronts when the product has enough of
+// them.  K advances 64 at a time through two LDS stages filled by
+// buffer_load_dwordx4 ... lds (no staging registers), with one barrier per
+// stage; the LDS operand reads of each 16-wide K step are issued while the
+// MFMAs of the previous step run.  Each stage buffer is its own LDS object,
+// so the compiler can tell a DMA into one stage from reads of the other and
+// does not wait on it.  LDS rows are 128 bytes (64 elements, eight 16-byte
 // chunks); chunk c of row r is stored at c ^ ((r >> 1) & 7), which spreads
 // the 16 rows of one 16-lane read phase over all 16 bank groups of gfx950's
 // 64-bank LDS.  Rows beyond M or N are clamped on load and masked on store.
@@ -27,8 +30,8 @@ namespace stb {
 
 namespace {
 
-constexpr int BM = 128, BN = 128;
-constexpr int kThreads = 256;
+// Fewest 256x256 tiles for which the large-tile configuration is used.
+constexpr int kBigTileMin = 192;
 
 // Output tile of this workgroup (1-D grid of mt * nt workgroups).
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
@@ -49,42 +52,6 @@ __device__ __forceinline__ void tile_coords(int mt, int nt, int bid, int& tm, in
   tm = first + (r - tn * gm);
 }
 
-
-// Head-split store of four consecutive rows (tokens) of one column.  For a
-// V^T destination the four values are contiguous and go out as one 8-byte
-// store when they belong to one sample and stay aligned.
-__device__ __forceinline__ void store_heads4(const HeadSplit& hs, int row0,
-                                             int col, const float v[4],
-                                             float bias, int M) {
-  const int which = col / hs.C;
-  const int s = which % hs.nsplit;
-  const int layer = which / hs.nsplit;
-  const int within = col - which * hs.C;
-  const int head = within >> 6;
-  const int dim = within & 63;
-  bf16_t* base = static_cast<bf16_t*>(hs.dst[s]) + layer * hs.layer_stride;
-  const bool trans = (hs.transposed_mask >> s) & 1;
-  const int b0 = row0 / hs.rows_per_batch;
-  const int n0 = row0 - b0 * hs.rows_per_batch;
-  if (trans && (hs.rows_per_batch & 3) == 0 && row0 + 3 < M) {
-    const long long bh = static_cast<long long>(b0) * hs.heads + head;
-    const uint2 pk = make_uint2(pack2bf(v[0] + bias, v[1] + bias),
-                                pack2bf(v[2] + bias, v[3] + bias));
-    *reinterpret_cast<uint2*>(base + (bh * kHeadDim + dim) * hs.npad + n0) = pk;
-    return;
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int row = row0 + k;
-    if (row >= M) break;
-    const int b = row / hs.rows_per_batch;
-    const int n = row - b * hs.rows_per_batch;
-    const long long bh = static_cast<long long>(b) * hs.heads + head;
-    const long long idx = trans ? (bh * kHeadDim + dim) * hs.npad + n
-                                : (bh * hs.npad + n) * kHeadDim + dim;
-    base[idx] = f2bf(v[k] + bias);
-  }
-}
 
 // Epilogue through LDS.  The wavefront's 64x64 fp32 tile is written to a
 // 16 KB LDS area in the accumulator layout, then read back along whichever
@@ -298,144 +265,176 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// Stage rows of BKT elements: 64 (128 bytes, eight chunks, chunk c of row r
-// at c ^ ((r >> 1) & 7)) or 32 (64 bytes, four chunks, at c ^ ((r >> 2) &
-// 3)); either way the 16 rows of one 16-lane read phase cover all 16 bank
-// groups of the 64-bank LDS.
-template <int BKT>
+// Offset (in elements) of 16-byte chunk `chunk` of stage row `row`: rows of
+// 64 elements, chunk c of row r at c ^ ((r >> 1) & 7), so that the 16 rows
+// of one 16-lane read phase cover all 16 bank groups of the 64-bank LDS.
 __device__ __forceinline__ int swz_k(int row, int chunk) {
-  if constexpr (BKT == 64)
-    return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
-  else
-    return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-template <int EPI, typename OpT, int BKT, int NST>
-__global__ __launch_bounds__(kThreads, 2) void gemm_dma_kernel(GemmParams p) {
-  // NST stage buffers per operand, each its own LDS object (see the file
-  // comment); unused ones are never referenced and take no LDS.
-  __shared__ __attribute__((aligned(16))) uint16_t sA0[BM * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sA1[BM * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sA2[BM * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sB0[BN * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sB1[BN * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sB2[BN * BKT];
-  static_assert(NST == 2 || NST == 3, "stages");
-  constexpr int RPB = 1024 / (BKT * 2);      // rows per 1 KB DMA block
-  constexpr int DPW = BM / RPB / 4;          // DMA blocks per wave per operand per stage
-  constexpr int CPR = BKT / 8;               // 16-byte chunks per row
+// buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes from `base` + soff + voff
+// into the 1 KB of LDS at `lds`, lane i landing in slot i.  Unlike
+// global_load_lds (a FLAT instruction, which the compiler must assume may
+// also be an LDS access), a buffer load leaves the LDS wait counter alone,
+// so the waits for LDS operand reads can stay partial.
+__device__ __forceinline__ void dma16(const void* base, int nbytes, uint16_t* lds,
+                                      unsigned voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+// ------------------------------------------------------ DMA-ring GEMM
+// WM x WN wavefronts, each owning (FM*32) x (FN*32) outputs as FM x FN MFMA
+// blocks; MINB workgroups per CU.  Stage k: wait for its DMA, barrier (every
+// wavefront is done with stage k-1), issue the DMA of stage k+1 into the
+// other buffers, then the four 16-wide K steps, the LDS operand reads of
+// step s+1 issued before the MFMAs of step s (two register sets; the
+// scheduling groups keep the compiler from folding them back into one).
+template <int EPI, typename OpT, int WM, int WN, int FM, int FN, int MINB>
+__global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
+  constexpr int BKT = 64;
+  constexpr int RPB = 8;                 // rows per 1 KB DMA block
+  constexpr int DPA = TBM / RPB / NW;    // A blocks per wavefront per stage
+  constexpr int DPB = TBN / RPB / NW;    // B blocks per wavefront per stage
+  static_assert(DPA * RPB * NW == TBM && DPB * RPB * NW == TBN, "DMA split");
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "epilogue works on 64x64 blocks");
+  static_assert(2 * (TBM + TBN) * BKT * 2 >= NW * 16384, "epilogue staging");
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[TBM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[TBM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[TBN * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[TBN * BKT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   // split-K: workgroup blockIdx.x takes tile blockIdx.x % tiles and K slice
   // blockIdx.x / tiles (always 0 without split)
-  const int mt = (p.M + BM - 1) / BM, nt = (p.N + BN - 1) / BN;
+  const int mt = (p.M + TBM - 1) / TBM, nt = (p.N + TBN - 1) / TBN;
   const int kz = blockIdx.x / (mt * nt);
   const int kslice = p.K / (p.ksplit > 1 ? p.ksplit : 1);
   int tm, tn;
   tile_coords(mt, nt, blockIdx.x - kz * mt * nt, tm, tn);
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  const int m0 = tm * TBM;
+  const int n0 = tn * TBN;
   const int M = p.M, N = p.N;
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* Bm = static_cast<const uint16_t*>(p.B);
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  // Lane i of a DMA block lands in slot i: row i / CPR, physical chunk
-  // i % CPR, so it fetches the logical chunk that belongs there.
-  long long aoff[DPW], boff[DPW];
+  // DMA through buffer loads: 32-bit byte offsets per lane, the K step as
+  // the scalar offset (callers keep each operand below 4 GB)
+  unsigned aoff[DPA], boff[DPB];
 #pragma unroll
-  for (int j2 = 0; j2 < DPW; ++j2) {
-    const int row = RPB * (wave * DPW + j2) + lane / CPR;
-    const int pc = lane % CPR;
-    const int cl = (BKT == 64) ? (pc ^ ((row >> 1) & 7)) : (pc ^ ((row >> 2) & 3));
-    aoff[j2] = static_cast<long long>(min(m0 + row, M - 1)) * p.lda + static_cast<long long>(kz) * kslice + cl * 8;
-    boff[j2] = static_cast<long long>(min(n0 + row, N - 1)) * p.ldb + static_cast<long long>(kz) * kslice + cl * 8;
+  for (int j2 = 0; j2 < DPA; ++j2) {
+    const int row = RPB * (wave * DPA + j2) + (lane >> 3);
+    const int cl = (lane & 7) ^ ((row >> 1) & 7);
+    aoff[j2] = static_cast<unsigned>((min(m0 + row, M - 1) * p.lda + kz * kslice + cl * 8) * 2);
   }
+#pragma unroll
+  for (int j2 = 0; j2 < DPB; ++j2) {
+    const int row = RPB * (wave * DPB + j2) + (lane >> 3);
+    const int cl = (lane & 7) ^ ((row >> 1) & 7);
+    boff[j2] = static_cast<unsigned>((min(n0 + row, N - 1) * p.ldb + kz * kslice + cl * 8) * 2);
+  }
+  const int abytes = M * static_cast<int>(p.lda) * 2, bbytes = N * static_cast<int>(p.ldb) * 2;
   auto issue = [&](int k, uint16_t* sa, uint16_t* sb) {
 #pragma unroll
-    for (int j2 = 0; j2 < DPW; ++j2) {
-      const int blk = (wave * DPW + j2) * 512;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(A + aoff[j2] + k * BKT),
-                                       (lds_ptr_t)(sa + blk), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Bm + boff[j2] + k * BKT),
-                                       (lds_ptr_t)(sb + blk), 16, 0, 0);
-    }
+    for (int j2 = 0; j2 < DPA; ++j2)
+      dma16(A, abytes, sa + (wave * DPA + j2) * 512, aoff[j2], k * BKT * 2);
+#pragma unroll
+    for (int j2 = 0; j2 < DPB; ++j2)
+      dma16(Bm, bbytes, sb + (wave * DPB + j2) * 512, boff[j2], k * BKT * 2);
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+  // operands of K step s (16 wide) of a stage
+  auto rd = [&](const uint16_t* sa, const uint16_t* sb, int s, uint4 (&a)[FM], uint4 (&b)[FN]) {
+    const int chunk = 2 * s + lhi;
 #pragma unroll
-    for (int s = 0; s < BKT / 16; ++s) {
-      const int chunk = 2 * s + lhi;
-      uint4 a[2], b[2];
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const uint4*>(sa + swz_k(wm * FM * 32 + i * 32 + l32, chunk));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const uint4*>(sa + swz_k<BKT>(wm * 64 + i * 32 + l32, chunk));
-        b[i] = *reinterpret_cast<const uint4*>(sb + swz_k<BKT>(wn * 64 + i * 32 + l32, chunk));
-      }
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const uint4*>(sb + swz_k(wn * FN * 32 + j * 32 + l32, chunk));
+  };
+  auto mm = [&](const uint4 (&a)[FM], const uint4 (&b)[FN]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j], OpT{});
-    }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j], OpT{});
   };
 
-  // Iteration k: stage k must have landed (later stages may still be in
-  // flight), every wavefront must be past iteration k-1 (whose buffer is
-  // refilled now with stage k + NST - 1), then stage k is consumed.
   const int nk = kslice / BKT;
-  constexpr int PER = 2 * DPW;  // DMA instructions per stage per wavefront
+  uint4 xa[FM], xb[FN], ya[FM], yb[FN];
   issue(0, sA0, sB0);
-  if (nk > 1 && NST > 2) issue(1, sA1, sB1);
-  auto step = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa,
-                  uint16_t* wb) {
-    if constexpr (NST == 3) {
-      if (k + 1 < nk) wait_vmcnt_lds<PER>();
-      else wait_vmcnt_lds<0>();
-    } else {
-      wait_vmcnt_lds<0>();
-    }
+  auto stage = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
+    wait_vmcnt_lds<0>();
     stage_barrier();
-    if (k + NST - 1 < nk) issue(k + NST - 1, wa, wb);
-    compute(ca, cb);
+    if (k + 1 < nk) issue(k + 1, wa, wb);
+    rd(ca, cb, 0, xa, xb);
+    rd(ca, cb, 1, ya, yb);
+    mm(xa, xb);
+    rd(ca, cb, 2, xa, xb);
+    mm(ya, yb);
+    rd(ca, cb, 3, ya, yb);
+    mm(xa, xb);
+    mm(ya, yb);
+    // keep the order: reads of step s+1 ahead of the MFMAs of step s
+    constexpr int R = FM + FN, F = FM * FN;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
   };
-  if constexpr (NST == 3) {
-    for (int k = 0; k < nk; k += 3) {
-      step(k, sA0, sB0, sA2, sB2);
-      if (k + 1 < nk) step(k + 1, sA1, sB1, sA0, sB0);
-      if (k + 2 < nk) step(k + 2, sA2, sB2, sA1, sB1);
-    }
-  } else {
-    for (int k = 0; k < nk; k += 2) {
-      step(k, sA0, sB0, sA1, sB1);
-      if (k + 1 < nk) step(k + 1, sA1, sB1, sA0, sB0);
-    }
+  for (int k = 0; k < nk; k += 2) {
+    stage(k, sA0, sB0, sA1, sB1);
+    if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
   }
 
   // every wavefront is done reading the stage buffers before they hold
   // the epilogue tiles
   stage_barrier();
-  float* stage = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1);
+  // 16 KB per wavefront: the stage buffers taken in order
+  float* stg_area;
+  {
+    constexpr int PA = TBM * BKT * 2 / 16384;  // wavefront areas per A buffer
+    constexpr int PB = TBN * BKT * 2 / 16384;
+    int w = wave;
+    if (w < PA) stg_area = reinterpret_cast<float*>(sA0) + w * 4096;
+    else if ((w -= PA) < PA) stg_area = reinterpret_cast<float*>(sA1) + w * 4096;
+    else if ((w -= PA) < PB) stg_area = reinterpret_cast<float*>(sB0) + w * 4096;
+    else stg_area = reinterpret_cast<float*>(sB1) + (w - PB) * 4096;
+  }
+  GemmParams q = p;
   if (p.ksplit > 1) {
     // this slice's product, plain fp32, into ws[kz]
-    GemmParams q = p;
     q.epi.kind = EPI_STORE_F32;
     q.epi.bias = nullptr;
     q.epi.out_f32 = p.ws + static_cast<long long>(kz) * M * N;
     q.epi.ldo = N;
-    epilogue_lds<EPI_STORE_F32>(q, acc, m0, n0, wm, wn, lane, stage);
-  } else {
-    epilogue_lds<EPI>(p, acc, m0, n0, wm, wn, lane, stage);
   }
+#pragma unroll
+  for (int si = 0; si < FM / 2; ++si)
+#pragma unroll
+    for (int sj = 0; sj < FN / 2; ++sj) {
+      const floatx16 sub[2][2] = {{acc[2 * si][2 * sj], acc[2 * si][2 * sj + 1]},
+                                  {acc[2 * si + 1][2 * sj], acc[2 * si + 1][2 * sj + 1]}};
+      const int r0 = m0 + wm * FM * 32 + si * 64, c0 = n0 + wn * FN * 32 + sj * 64;
+      if (p.ksplit > 1) epilogue_lds<EPI_STORE_F32>(q, sub, r0, c0, 0, 0, lane, stg_area);
+      else epilogue_lds<EPI>(p, sub, r0, c0, 0, 0, lane, stg_area);
+    }
 }
 
 // Second pass of split-K: the slices added in order (deterministic), then
@@ -498,26 +497,45 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 
 }  // namespace
 
-#ifndef ST_GEMM_BKT
-#define ST_GEMM_BKT 64
-#endif
-#ifndef ST_GEMM_NST
-#define ST_GEMM_NST 2
-#endif
-constexpr int kBKT = ST_GEMM_BKT, kNST = ST_GEMM_NST;
+namespace {
+template <int WM, int WN, int FM, int FN, int MINB>
+hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStream_t s) {
+  constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
+  const dim3 grid(((p.M + TBM - 1) / TBM) * ((p.N + TBN - 1) / TBN) * split);
+  constexpr int threads = 64 * WM * WN;
+#define ST_PIPE_CASE(E)                                                                          \
+  case E:                                                                                        \
+    if (op == ACT_F16) gemm_pipe_kernel<E, f16_t, WM, WN, FM, FN, MINB><<<grid, threads, 0, s>>>(p); \
+    else gemm_pipe_kernel<E, bf16_t, WM, WN, FM, FN, MINB><<<grid, threads, 0, s>>>(p);          \
+    break;
+  switch (kind) {
+    ST_PIPE_CASE(EPI_STORE_F32)
+    ST_PIPE_CASE(EPI_RESID_F32)
+    ST_PIPE_CASE(EPI_HEADS)
+    ST_PIPE_CASE(EPI_GEGLU)
+    ST_PIPE_CASE(EPI_NCHW)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef ST_PIPE_CASE
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (p.K % kBKT) return hipErrorInvalidValue;
-  const int split = p.ksplit > 1 ? p.ksplit : 1;
-  if (split > 1 && (!p.ws || p.K % (split * kBKT) || op != ACT_BF16 ||
-                    (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32)))
+  if (p.K % 64) return hipErrorInvalidValue;
+  // the DMA addresses each operand with 32-bit byte offsets
+  if (static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL ||
+      static_cast<long long>(p.N) * p.ldb * 2 > 0x7fffffffLL)
     return hipErrorInvalidValue;
-  const dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM) * split);
+  const int split = p.ksplit > 1 ? p.ksplit : 1;
   if (split > 1) {
+    if (!p.ws || p.K % (split * 64) || op != ACT_BF16 ||
+        (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))
+      return hipErrorInvalidValue;
     // the slices (the kernel switches to the plain fp32 store), then the sum
-    gemm_dma_kernel<EPI_STORE_F32, bf16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, split, s);
     if (e != hipSuccess) return e;
     const long long mn = static_cast<long long>(p.M) * p.N;
     const unsigned blocks = static_cast<unsigned>((mn + 255) / 256);
@@ -525,22 +543,11 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
     else splitk_reduce_kernel<EPI_STORE_F32><<<blocks, 256, 0, s>>>(p);
     return hipGetLastError();
   }
-#define ST_GEMM_CASE(E)                                                     \
-  case E:                                                                   \
-    if (op == ACT_F16) gemm_dma_kernel<E, f16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p); \
-    else gemm_dma_kernel<E, bf16_t, kBKT, kNST><<<grid, kThreads, 0, s>>>(p);           \
-    break;
-  switch (p.epi.kind) {
-    ST_GEMM_CASE(EPI_STORE_F32)
-    ST_GEMM_CASE(EPI_RESID_F32)
-    ST_GEMM_CASE(EPI_HEADS)
-    ST_GEMM_CASE(EPI_GEGLU)
-    ST_GEMM_CASE(EPI_NCHW)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef ST_GEMM_CASE
-  return hipGetLastError();
+  // 256x256 tiles (eight wavefronts of 128x64) when there are enough of
+  // them to give most CUs one; otherwise 128x128 tiles, two per CU.
+  const long long big_tiles = static_cast<long long>((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big_tiles >= kBigTileMin) return launch_pipe<2, 4, 4, 2, 1>(p, op, p.epi.kind, 1, s);
+  return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
 }
 
 hipError_t gemm_f32(const GemmParams& p, hipStream_t s) {
