@@ -66,6 +66,25 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Wavefront sum without LDS: DPP within each row of 16 lanes (swap
+// neighbours, swap pairs, half-row mirror, row mirror: every lane then holds
+// its row's sum), then row_bcast15 / row_bcast31 carry the row sums up to
+// lane 63, whose value is broadcast.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xF>(v);  // row_mirror
+  v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -210,9 +210,9 @@ hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
 }
 
 // ---------------------------------------------------------------- LayerNorm
-// One wavefront per token row of the fp32 residual stream; the row is held in
-// registers (VPL float4 per lane), mean and variance are two exact passes
-// over registers with wavefront butterfly reductions.
+// One wavefront per token row of the fp32 residual stream; the row, gamma and
+// beta are held in registers (VPL float4 each per lane), mean and variance
+// are two exact passes over registers with wavefront sums in registers.
 template <int VPL, typename TO>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const float* __restrict__ h, const float* __restrict__ gamma,
@@ -222,15 +222,22 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   if (row >= T) return;
   const float4* hr = reinterpret_cast<const float4*>(h + static_cast<long long>(row) * C);
   const int nv = C / 4;
-  float4 v[VPL];
-  float s = 0.f;
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  const float4* b4 = reinterpret_cast<const float4*>(beta);
+  // the row, gamma and beta all in flight at once
+  float4 v[VPL], g[VPL], bb[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = lane + 64 * i;
-    v[i] = j < nv ? hr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const bool in = j < nv;
+    v[i] = in ? hr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    g[i] = in ? g4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    bb[i] = in ? b4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float mean = warp_sum(s) / C;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float mean = wave_sum(s) / C;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -240,18 +247,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
       q += (a * a + b * b) + (c * c + d * d);
     }
   }
-  const float rstd = rsqrtf(warp_sum(q) / C + 1e-5f);
-  const float4* g4 = reinterpret_cast<const float4*>(gamma);
-  const float4* b4 = reinterpret_cast<const float4*>(beta);
+  const float rstd = rsqrtf(wave_sum(q) / C + 1e-5f);
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = lane + 64 * i;
     if (j < nv) {
-      float4 g = g4[j], bb = b4[j];
-      float o0 = (v[i].x - mean) * rstd * g.x + bb.x;
-      float o1 = (v[i].y - mean) * rstd * g.y + bb.y;
-      float o2 = (v[i].z - mean) * rstd * g.z + bb.z;
-      float o3 = (v[i].w - mean) * rstd * g.w + bb.w;
+      float o0 = (v[i].x - mean) * rstd * g[i].x + bb[i].x;
+      float o1 = (v[i].y - mean) * rstd * g[i].y + bb[i].y;
+      float o2 = (v[i].z - mean) * rstd * g[i].z + bb[i].z;
+      float o3 = (v[i].w - mean) * rstd * g[i].w + bb[i].w;
       TO* dst = u + static_cast<long long>(row) * C + 4 * j;
       if constexpr (sizeof(TO) == 2) {
         uint2 pk = make_uint2(pack2<TO>(o0, o1), pack2<TO>(o2, o3));
