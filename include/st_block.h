@@ -141,7 +141,8 @@ const char *st_last_error(void);
  * Per-kernel timing.  st_block_set_timing(blk, mask) selects kernel kinds by
  * bit (1u << st_kernel_kind; 0 = off).  Every later forward records a pair of
  * HIP events around each launch of a selected kind, on the stream the kernel
- * is launched on.  After the caller has synchronised that stream,
+ * is launched on (events without the system-scope fence: they time, they
+ * do not synchronise).  After the caller has synchronised that stream,
  * st_block_read_timing() adds the elapsed times up by kind (milliseconds
  * summed over every forward since the last read, and launch counts) and
  * clears them.  Selecting fewer kinds perturbs the other kernels less.

@@ -27,7 +27,7 @@ __device__ __forceinline__ void store_heads(const HeadSplit& hs, int row,
     idx = (bh * kHeadDim + dim) * hs.npad + n;
   else
     idx = (bh * hs.npad + n) * kHeadDim + dim;
-  base[idx] = from_f32<TA>(v);
+  base[idx] = from_f32<TA>(v * hs.scale[s]);
 }
 
 template <int EPI, typename TA>

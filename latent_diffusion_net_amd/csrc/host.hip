@@ -443,7 +443,11 @@ hipEvent_t take_event(st_block* b) {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) {
+  // Timing only: without the system-scope fence, recording an event does not
+  // write back and invalidate the caches (a gap of several microseconds
+  // between kernels on a multi-XCD GPU otherwise); the caller synchronises
+  // its stream before the times are read.
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
@@ -475,6 +479,7 @@ GemmParams gemm(const void* A, long long lda, const void* Bm, long long ldb,
   p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb;
   p.M = M; p.N = N; p.K = K;
   p.epi.kind = kind;
+  for (float& v : p.epi.hs.scale) v = 1.f;
   return p;
 }
 
@@ -536,6 +541,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              GemmParams p = gemm(b->u, C, L.wqkv, C, T, 3 * C, C, EPI_HEADS);
              p.epi.bias = L.bqkv;
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = b->k; p.epi.hs.dst[2] = b->vt;
+             if (bf) p.epi.hs.scale[0] = attention_bf16_q_scale();
              p.epi.hs.transposed_mask = 4; p.epi.hs.nsplit = 3; p.epi.hs.layer_stride = 0;
              p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
              p.epi.hs.heads = b->heads; p.epi.hs.C = C;
@@ -565,6 +571,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              GemmParams p = gemm(b->u, C, L.wq2, C, T, C, C, EPI_HEADS);
              p.epi.bias = L.bq2;
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = nullptr; p.epi.hs.dst[2] = nullptr;
+             if (bf) p.epi.hs.scale[0] = attention_bf16_q_scale();
              p.epi.hs.transposed_mask = 0; p.epi.hs.nsplit = 1; p.epi.hs.layer_stride = 0;
              p.epi.hs.rows_per_batch = N; p.epi.hs.npad = b->npad;
              p.epi.hs.heads = b->heads; p.epi.hs.C = C;

@@ -13,8 +13,13 @@
 // the output stay in the lane, and only the row max needs one exchange with
 // the other lane half.  The probabilities then feed O^T += V^T P^T directly
 // as the B operand of the second MFMA, in the same K order that the V^T
-// operand is read from LDS.  Softmax runs in fp32 with exp2 and the scale
-// 1/8 * log2(e) folded into one FMA; keys at or beyond Nk get -inf.
+// operand is read from LDS.  Softmax runs in fp32 with exp2: the queries
+// arrive multiplied by log2(e)/8 (the projection's epilogue does it), and
+// each score block starts with one more MFMA step that adds -m, the row's
+// reference max, so that the accumulators already hold the exponents and the
+// vector units do no per-score arithmetic before exp2.  m is kept
+// representable in bf16, so that this step adds it exactly.  Keys at or
+// beyond Nk get -inf.
 //
 // fp32 path (debug builds): one thread per query row, K/V tiles in LDS,
 // online softmax in fp32.
@@ -159,8 +164,16 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
       for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
   float mref[QB], lsum[QB];  // lsum: this lane's partial row sums
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
-  const float c = 0.125f * kLog2e;
+  for (int qb = 0; qb < QB; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
+  // The max step of the score MFMAs: A = a column of ones (dimension 0 of
+  // lane half 0), B = -m of the lane's query in the same dimension.
+  const uint4 ones_col = lhi == 0 ? make_uint4(0x3F80u, 0u, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+  uint4 negm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) negm[qb] = make_uint4(0u, 0u, 0u, 0u);
+  auto set_negm = [&](int qb) {
+    negm[qb].x = lhi == 0 ? static_cast<uint32_t>(f2bf(-mref[qb])) : 0u;
+  };
   // Byte offset of this lane's operand chunk for step s within a 32-row half
   // tile; rows 32..63 add 4096 bytes (the swizzle key depends on row bits 1-3
   // only).  The empty asm hides how the offset is formed, so that the buffer
@@ -182,9 +195,12 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        floatx16 z;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) z[r] = 0.f;
+        sc[qb][kb] = mfma32x32x16(ones_col, negm[qb], z, bf16_t{});
+      }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -196,8 +212,9 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
       }
   };
 
-  // Exact row max of the tile: raises the reference max and rescales the
-  // running sum and output.
+  // Exact row max of the tile, whose scores are relative to the reference
+  // max m: raises m by the (bf16-rounded) excess, rescales the running sum
+  // and output by 2^-excess and shifts the tile's scores to the new m.
   auto exact_max = [&](floatx16 (&sc)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -207,14 +224,38 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(mref[qb], mt);
-      const float alpha = __builtin_amdgcn_exp2f((mref[qb] - m_new) * c);
+      const float m_new = bf2f(f2bf(mref[qb] + fmaxf(mt, 0.f)));
+      const float delta = m_new - mref[qb];
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
       mref[qb] = m_new;
+      set_negm(qb);
       lsum[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][kb][r] -= delta;
+    }
+  };
+  // The first tile sets m from its own max (whatever its sign).
+  auto first_max = [&](floatx16 (&sc)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mt = sc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[qb][kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mref[qb] = bf2f(f2bf(mt));
+      set_negm(qb);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][kb][r] -= mref[qb];
     }
   };
   // Probabilities of a tile against the reference max, as packed bf16 B
@@ -229,7 +270,6 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     one[1] = static_cast<__bf16>(1.0f);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mc = mref[qb] * c;
       ps[qb] = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -237,8 +277,8 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           bf16x2 pk;
-          pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[qb][st >> 1][8 * (st & 1) + 2 * j], c, -mc)));
-          pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[qb][st >> 1][8 * (st & 1) + 2 * j + 1], c, -mc)));
+          pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[qb][st >> 1][8 * (st & 1) + 2 * j]));
+          pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[qb][st >> 1][8 * (st & 1) + 2 * j + 1]));
           ps[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ps[qb], false);
           w[j] = __builtin_bit_cast(uint32_t, pk);
         }
@@ -299,10 +339,11 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   stage_barrier();
   qk(sK0, sc);
   if (ragged_last == kt0) mask_tile(kt0, sc);
-  exact_max(sc);
+  first_max(sc);
   stage_barrier();  // every wavefront is done with K_0 before K_3 replaces it
 
   constexpr int kIssued = 2 * BPW;  // DMA instructions per wavefront per iteration
+  const int tlast = kt1 - 1;
   auto iter = [&](int t, const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
     if (t + 3 < ntiles) issue_k(kt0 + t + 3, kw);
     if (t + 2 < ntiles) issue_v(kt0 + t + 2, vw);
@@ -333,8 +374,11 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
     iter(t + 1, sK2, sV1, sK1, sV0);
     iter(t + 2, sK0, sV2, sK2, sV1);
   }
-  if (t < ntiles) iter(t, sK1, sV0, sK0, sV2);
-  if (t + 1 < ntiles) iter(t + 1, sK2, sV1, sK1, sV0);
+  if (t < ntiles) {
+    iter(t, sK1, sV0, sK0, sV2);
+    if (t + 1 < ntiles) iter(t + 1, sK2, sV1, sK1, sV0);
+  }
+  wait_vmcnt_lds<0>();  // no DMA may still write LDS when the workgroup ends
 
   // Row sums over both lane halves.  Lane l holds O^T entries of query
   // q0 + 32qb + l32, dims db*32 + 8g + 4*lhi + 0..3 (g = r / 4).
@@ -387,12 +431,12 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 
 // Second pass of the key split: for each split query tile, the pieces'
 // partial results are merged in piece order (bitwise reproducible):
-// O = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^((m_i - max_i m_i) c).
+// O = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_i m_i) (the
+// references m_i are base-2 exponents).
 // Two threads per query row, 32 dims each.
 template <int QT>
 __global__ __launch_bounds__(2 * QT) void attn_merge_kernel(AttnParams p) {
   constexpr int PF = QT * 66;
-  const float c = 0.125f * kLog2e;
   const int j = blockIdx.x;  // split tile index
   const int tile = p.n_full + j;
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
@@ -410,7 +454,7 @@ __global__ __launch_bounds__(2 * QT) void attn_merge_kernel(AttnParams p) {
   float den = 0.f;
   for (int i = 0; i < p.nsplit; ++i) {
     const float* pi = tp + i * PF;
-    const float w = __builtin_amdgcn_exp2f((pi[QT * 64 + row] - mmax) * c);
+    const float w = __builtin_amdgcn_exp2f(pi[QT * 64 + row] - mmax);
     den += pi[QT * 65 + row] * w;
     const float4* src = reinterpret_cast<const float4*>(pi + row * 64 + half * 32);
 #pragma unroll
@@ -496,6 +540,7 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(AttnParams p) {
 
 int attention_bf16_q_tile() { return kQT; }
 int attention_bf16_kv_tile() { return KT; }
+float attention_bf16_q_scale() { return 0.125f * kLog2e; }
 int attention_bf16_part_floats() { return kQT * 66; }
 
 void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full, int& nsplit) {

@@ -157,6 +157,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
     const int head = (C0 - which * hs.C) >> 6;
     bf16_t* base = static_cast<bf16_t*>(hs.dst[sp]) + layer * hs.layer_stride;
     const float* bias = p.epi.bias ? p.epi.bias + C0 : nullptr;
+    const float sc = hs.scale[sp];
     if (!((hs.transposed_mask >> sp) & 1)) {
       // [bh][n][64]: lane -> 4 consecutive dims of one token
       const int lc = (lane & 15) * 4;
@@ -171,7 +172,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         const int b = row / hs.rows_per_batch;
         const int n = row - b * hs.rows_per_batch;
         const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
-        const uint2 pk = make_uint2(pack2bf(c.x + bb[0], c.y + bb[1]), pack2bf(c.z + bb[2], c.w + bb[3]));
+        const uint2 pk = make_uint2(pack2bf((c.x + bb[0]) * sc, (c.y + bb[1]) * sc),
+                                    pack2bf((c.z + bb[2]) * sc, (c.w + bb[3]) * sc));
         const long long bh = static_cast<long long>(b) * hs.heads + head;
         *reinterpret_cast<uint2*>(base + (bh * hs.npad + n) * kHeadDim + lc) = pk;
       }
@@ -187,7 +189,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         if (row0 >= M) break;
         float v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = stage[stg(lr0 + k, dim)] + bb;
+        for (int k = 0; k < 4; ++k) v[k] = (stage[stg(lr0 + k, dim)] + bb) * sc;
         if (vec && row0 + 3 < M) {
           const int b = row0 / hs.rows_per_batch;
           const int n = row0 - b * hs.rows_per_batch;

@@ -21,9 +21,11 @@ enum EpiKind {
 // (col % C) / 64, dim = col % 64; row maps to sample b = row / rows_per_batch
 // and sequence position n = row % rows_per_batch.  dst[s] + layer*layer_stride
 // is a [B*heads][npad][64] array, or [B*heads][64][npad] when bit s of
-// transposed_mask is set.
+// transposed_mask is set.  Values of split s (bias included) are multiplied
+// by scale[s] before rounding.
 struct HeadSplit {
   void* dst[3];
+  float scale[3];
   int transposed_mask;
   int nsplit;
   long long layer_stride;
@@ -88,7 +90,11 @@ struct AttnParams {
   int n_full, nsplit;
   float* part;        // [tiles - n_full][nsplit][attention_bf16_part_floats()]
 };
+// bf16 path: q holds the queries already multiplied by
+// attention_bf16_q_scale() = log2(e) / sqrt(64), so that the kernel's scores
+// are base-2 exponents.
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s);
+float attention_bf16_q_scale();
 hipError_t attention_f32(const AttnParams& p, hipStream_t s);
 int attention_bf16_q_tile();   // query rows per workgroup of the bf16 kernel
 int attention_bf16_kv_tile();  // key rows per LDS tile of the bf16 kernel
