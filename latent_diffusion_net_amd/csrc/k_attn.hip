@@ -17,9 +17,9 @@
 // arrive multiplied by log2(e)/8 (the projection's epilogue does it), and
 // each score block starts with one more MFMA step that adds -m, the row's
 // reference max, so that the accumulators already hold the exponents and the
-// vector units do no per-score arithmetic before exp2.  m is kept
-// representable in bf16, so that this step adds it exactly.  Keys at or
-// beyond Nk get -inf.
+// vector units do no per-score arithmetic before exp2.  m is kept equal to
+// the sum of two bf16 values (hi + lo, ~16 significant bits), which this
+// step adds exactly.  Keys at or beyond Nk get -inf.
 //
 // fp32 path (debug builds): one thread per query row, K/V tiles in LDS,
 // online softmax in fp32.
@@ -165,14 +165,18 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   float mref[QB], lsum[QB];  // lsum: this lane's partial row sums
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
-  // The max step of the score MFMAs: A = a column of ones (dimension 0 of
-  // lane half 0), B = -m of the lane's query in the same dimension.
-  const uint4 ones_col = lhi == 0 ? make_uint4(0x3F80u, 0u, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+  // The max step of the score MFMAs: A = ones in dimensions 0 and 1 (lane
+  // half 0), B = -m_hi, -m_lo of the lane's query in the same dimensions.
+  const uint4 ones_col = lhi == 0 ? make_uint4(0x3F803F80u, 0u, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
   uint4 negm[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) negm[qb] = make_uint4(0u, 0u, 0u, 0u);
-  auto set_negm = [&](int qb) {
-    negm[qb].x = lhi == 0 ? static_cast<uint32_t>(f2bf(-mref[qb])) : 0u;
+  // m := hi + lo with hi = bf16(x), lo = bf16(x - hi); exact in fp32.
+  auto set_m = [&](int qb, float x) {
+    const uint32_t hi = f2bf(x);
+    const uint32_t lo = f2bf(x - bf2f(hi));
+    mref[qb] = bf2f(hi) + bf2f(lo);
+    negm[qb].x = lhi == 0 ? ((hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16)) : 0u;
   };
   // Byte offset of this lane's operand chunk for step s within a 32-row half
   // tile; rows 32..63 add 4096 bytes (the swizzle key depends on row bits 1-3
@@ -213,8 +217,8 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
   };
 
   // Exact row max of the tile, whose scores are relative to the reference
-  // max m: raises m by the (bf16-rounded) excess, rescales the running sum
-  // and output by 2^-excess and shifts the tile's scores to the new m.
+  // max m: raises m by the excess (rounded to hi + lo), rescales the running
+  // sum and output by 2^-excess and shifts the tile's scores to the new m.
   auto exact_max = [&](floatx16 (&sc)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -224,11 +228,10 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = bf2f(f2bf(mref[qb] + fmaxf(mt, 0.f)));
-      const float delta = m_new - mref[qb];
+      const float m_old = mref[qb];
+      set_m(qb, m_old + fmaxf(mt, 0.f));
+      const float delta = mref[qb] - m_old;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
-      mref[qb] = m_new;
-      set_negm(qb);
       lsum[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
@@ -250,8 +253,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      mref[qb] = bf2f(f2bf(mt));
-      set_negm(qb);
+      set_m(qb, mt);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
