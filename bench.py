@@ -33,6 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "self_attn_sdxl_down1_hbm_traffic.
 COPY_BYTES = 256 << 20      # calibration copy: 256 MiB read + 256 MiB written
 SELF_ATTN_KERNEL = "attn_bf16_kernel<0,"   # kernel-name prefix of self-attention
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 DEFAULT_WORKLOAD = 3       # index into synth.CONFIGS: SDXL Down1, 64x64, depth 2
 
 
@@ -47,6 +48,66 @@ def block_flops(cfg) -> float:
     per_layer = 36.0 * T * C * C + attention_flops(cfg) + 4.0 * B * N * 77 * C \
         + 4.0 * B * 77 * D * C
     return 4.0 * T * C * C + depth * per_layer
+
+
+# Algorithmic work per launch of each timed kernel kind, and the roofline
+# that bounds it: (row(s) of the method, bound, work per launch).  Flops count
+# 2 per multiply-add; bytes count what the step must read and write at least
+# once (bf16 storage).  proj_in's time also holds the GroupNorm apply, and
+# proj_out is charged its algorithmic 2*T*C^2 (the bf16 path runs it with K
+# doubled: h enters as two bf16 terms).
+def row_work(cfg):
+    T, C, B, N, D, F, h = cfg.T, cfg.C, cfg.B, cfg.N, cfg.D_ctx, cfg.F, cfg.heads
+    return {
+        "gn_stats": ("A1 GroupNorm statistics", "hbm", 2.0 * T * C),
+        "proj_in": ("A2 GroupNorm apply + proj_in", "mfma", 2.0 * T * C * C),
+        "layernorm": ("A3/A7/A12 LayerNorm", "hbm", T * C * (4.0 + 2.0)),
+        "qkv": ("A4 Q/K/V projection", "mfma", 6.0 * T * C * C),
+        "self_attn": ("A5 self-attention", "mfma", attention_flops(cfg)),
+        "attn_out": ("A6/A11 out-projections + residual", "mfma", 2.0 * T * C * C),
+        "cross_q": ("A8 cross-attention Q", "mfma", 2.0 * T * C * C),
+        "ctx_kv": ("A9 context K/V (all layers)", "mfma", 2.0 * B * 77 * 2 * C * cfg.depth * D),
+        "cross_attn": ("A10 cross-attention", "hbm", 2.0 * T * C * 2 + 2.0 * B * h * 77 * 64 * 2),
+        "ff1_geglu": ("A13 FF1 + GEGLU", "mfma", 16.0 * T * C * C),
+        "ff2": ("A14 FF2 + residual", "mfma", 8.0 * T * C * C),
+        "proj_out": ("A15 proj_out + NCHW + residual", "mfma", 2.0 * T * C * C),
+    }
+
+
+def copy_ceiling_gbs(torch, dev):
+    """Device-to-device copy rate of a 256 MiB buffer (read + write bytes)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del src, dst
+    return 2.0 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def row_rates(cfg, timing, copy_gbs):
+    rows = {}
+    for kind, (name, bound, work) in row_work(cfg).items():
+        t = timing.get(kind)
+        if not t or not t["launches"]:
+            continue
+        s = t["ms"] / 1e3 / t["launches"]
+        if bound == "hbm":
+            a = work / s / 1e9
+            rows[name] = {"bound": "hbm", "achieved": round(a, 1), "unit": "GB/s",
+                          "peak": HBM_PEAK_GBS, "frac": round(a / HBM_PEAK_GBS, 3),
+                          "frac_of_copy": round(a / copy_gbs, 3), "us_per_launch": round(s * 1e6, 2)}
+        else:
+            a = work / s / 1e12
+            rows[name] = {"bound": "mfma", "achieved": round(a, 1), "unit": "TFLOP/s",
+                          "peak": BF16_PEAK_TFLOPS, "frac": round(a / BF16_PEAK_TFLOPS, 3),
+                          "us_per_launch": round(s * 1e6, 2)}
+    return rows
 
 
 def source_hash() -> str:
@@ -121,7 +182,7 @@ def main():
                     help="workload index (default: the SDXL Down1 block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
-                    help="also time every kernel kind in an extra untimed pass")
+                    help="also print the per-step microseconds of every kernel kind")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection run: a 256 MiB device copy (the "
                          "calibration kernel) then a few forwards; no JSON")
@@ -187,17 +248,20 @@ def main():
     attn_s = attn["ms"] / 1e3 / attn["launches"]
     attn_tflops = attention_flops(cfg) / attn_s / 1e12
 
-    kernels = None
-    if args.kernels:
-        from latent_diffusion_net_amd.binding import KERNEL_KINDS
-        blk.set_timing(KERNEL_KINDS)
-        for _ in range(5):
-            blk.forward(x, ctx, y, stream)
-        torch.cuda.synchronize()
-        kt = blk.read_timing()
-        blk.set_timing([])
-        kernels = {k: round(v["ms"] / 5 * 1e3, 2) for k, v in kt.items()}
+    # Every kernel kind against its roofline, from a few more forwards after
+    # the timed region (events around every launch perturb the block rate,
+    # so they stay out of it).
+    from latent_diffusion_net_amd.binding import KERNEL_KINDS
+    blk.set_timing(KERNEL_KINDS)
+    for _ in range(5):
+        blk.forward(x, ctx, y, stream)
+    torch.cuda.synchronize()
+    kt = blk.read_timing()
+    blk.set_timing([])
+    kernels = {k: round(v["ms"] / 5 * 1e3, 2) for k, v in kt.items()} if args.kernels else None
     blk.close()
+    copy_gbs = copy_ceiling_gbs(torch, dev)
+    rows = row_rates(cfg, kt, copy_gbs)
 
     result = {
         "metric": METRIC,
@@ -223,6 +287,8 @@ def main():
                      "us_per_launch": attn_s * 1e6,
                      "flops_per_launch": attention_flops(cfg)},
         "block_tflops": block_flops(cfg) / (dt / args.steps) / 1e12,
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "rows": rows,
     }
     if kernels is not None:
         result["kernel_us_per_step"] = kernels

@@ -84,3 +84,35 @@ def test_traffic_figure_is_tied_to_the_kernel_source(bench, tmp_path, monkeypatc
     src.write_text("// kernel v2\n")                  # source changed
     assert bench.measured_traffic() is None
 
+
+
+def test_row_work_adds_up_to_block_flops(bench):
+    """The per-kernel work of the roofline rows, counted per forward, plus the
+    cross-attention contractions (charged to the HBM-bound row by bytes)
+    is every FLOP of the block."""
+    from latent_diffusion_net_amd import synth
+    for cfg in synth.CONFIGS:
+        work = bench.row_work(cfg)
+        per_forward = {"proj_in": 1, "proj_out": 1, "ctx_kv": 1}
+        for k in ("qkv", "self_attn", "cross_q", "ff1_geglu", "ff2"):
+            per_forward[k] = cfg.depth
+        per_forward["attn_out"] = 2 * cfg.depth
+        total = sum(work[k][2] * n for k, n in per_forward.items())
+        assert all(work[k][1] == "mfma" for k in per_forward)
+        cross = cfg.depth * 4.0 * cfg.B * cfg.N * 77 * cfg.C
+        assert abs(total + cross - bench.block_flops(cfg)) <= 1e-9 * bench.block_flops(cfg)
+
+
+def test_row_rates_units(bench):
+    from latent_diffusion_net_amd import synth
+    cfg = synth.CONFIGS[3]
+    t = {"self_attn": {"ms": 0.2, "launches": 2}, "layernorm": {"ms": 0.036, "launches": 6},
+         "qkv": {"ms": 0.0, "launches": 0}}
+    r = bench.row_rates(cfg, t, 5000.0)
+    a = r["A5 self-attention"]
+    assert a["unit"] == "TFLOP/s" and a["us_per_launch"] == 100.0
+    assert abs(a["achieved"] - bench.attention_flops(cfg) / 100e-6 / 1e12) < 0.1
+    ln = r["A3/A7/A12 LayerNorm"]
+    assert ln["unit"] == "GB/s" and abs(ln["achieved"] - cfg.T * cfg.C * 6 / 6e-6 / 1e9) < 0.1
+    assert abs(ln["frac_of_copy"] - ln["achieved"] / 5000.0) < 1e-3
+    assert "A4 Q/K/V projection" not in r  # no launches: no row
