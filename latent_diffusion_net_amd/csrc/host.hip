@@ -17,8 +17,8 @@
 //     out-projection GEMM           O, Wo2                -> h += .
 //     LayerNorm 3, FF1 GEMM+GEGLU   h, W1 (repacked)      -> f [T][F] bf16
 //     FF2 GEMM                      f, W2                 -> h += .
-//   proj_out GEMM, transposed       [W_out|W_out], h hi|lo -> y = NCHW(.) + x
-//     (the last FF2 also writes h as bf16 hi + lo terms, [T][2C])
+//   proj_out GEMM, transposed       W_out, h (fp16 copy)  -> y = NCHW(.) + x
+//     (the last FF2 also writes h as fp16, [T][C])
 // The fp32 debug path runs the same schedule with fp32 buffers and kernels,
 // GEGLU as its own pass.
 #include <hip/hip_runtime.h>
@@ -92,7 +92,7 @@ struct st_block {
   size_t bytes_cap;
 
   float *gn_w, *gn_b;
-  void *w_in, *w_out;  // bf16 path: w_out is [C][2C], the weight twice along K
+  void *w_in, *w_out;
   float *b_in, *b_out;
   std::vector<LayerDev> L;
   void* wkv;  // [depth*2C][D]: per layer Wk2 rows then Wv2 rows
@@ -102,7 +102,7 @@ struct st_block {
   int gn_max_split;
   void* u;
   float* h;
-  void* hsplit;  // bf16 path: [T][2C] bf16, h = hi + lo (hi in [0,C), lo in [C,2C))
+  void* hcopy;  // bf16 path: [T][C] fp16 copy of the last h, proj_out's operand
   void *q, *k, *vt, *o, *f;
   float* z;  // fp32 path: FF1 output before GEGLU
   void *kc, *vct;
@@ -271,16 +271,8 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->w_in = cr.mat(w->proj_in_w, C, C, "proj_in_w");
   cr.to_f16(b->w_in, CC, "proj_in_w to fp16");
   b->b_in = cr.vec(w->proj_in_b, C, 0.f, "proj_in_b");
-  if (b->bf16) {
-    // [W_out | W_out]: proj_out multiplies it with [h_hi | h_lo] (K = 2C)
-    b->w_out = cr.alloc(2 * CC * es, "proj_out_w");
-    for (int half = 0; half < 2 && cr.ok(); ++half)
-      cr.dev(hipMemcpy2DAsync(static_cast<char*>(b->w_out) + half * C * es, 2 * C * es,
-                              w->proj_out_w, C * es, C * es, C, hipMemcpyDeviceToDevice, s),
-             "proj_out_w");
-  } else {
-    b->w_out = cr.mat(w->proj_out_w, C, C, "proj_out_w");
-  }
+  b->w_out = cr.mat(w->proj_out_w, C, C, "proj_out_w");
+  cr.to_f16(b->w_out, CC, "proj_out_w to fp16");
   b->b_out = cr.vec(w->proj_out_b, C, 0.f, "proj_out_b");
 
   // Context K/V weights of every layer in one matrix.
@@ -360,7 +352,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->gn_part = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split, "GroupNorm partials"));
   b->u = cr.alloc(T * C * es, "normalised activations");
   b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
-  b->hsplit = b->bf16 ? cr.alloc(T * 2LL * C * es, "split residual stream") : nullptr;
+  b->hcopy = b->bf16 ? cr.alloc(T * static_cast<long long>(C) * es, "fp16 residual stream") : nullptr;
   const long long headbuf = static_cast<long long>(B) * heads * b->npad * 64 * es;
   b->q = cr.alloc(headbuf, "Q");
   b->k = cr.alloc(headbuf, "K");
@@ -613,8 +605,8 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_FF2, s, [&] {
              GemmParams p = gemm(b->f, F, L.w2, F, T, C, F, EPI_RESID_F32);
              p.epi.bias = L.b2; p.epi.out_f32 = b->h; p.epi.ldo = C;
-             // the last layer also leaves h as two bf16 terms for proj_out
-             if (bf && l + 1 == b->depth && stop_stage < 0) p.epi.out_act = b->hsplit;
+             // the last layer also leaves h as fp16 for proj_out
+             if (bf && l + 1 == b->depth && stop_stage < 0) p.epi.out_act = b->hcopy;
              return G(p, ACT_F16);
            }), "feed-forward 2");
     ++stage;
@@ -628,14 +620,12 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   }
   ST_TRY(run(b, ST_K_PROJ_OUT, s, [&] {
            // y^T orientation: rows = channels, columns = tokens, so the NCHW
-           // store is contiguous along tokens.
-           // bf16: y^T = [W_out | W_out] [h_hi | h_lo]^T, K = 2C, so that
-           // the fp32 residual stream enters with ~16 significant bits.
-           GemmParams p = bf ? gemm(b->w_out, 2 * C, b->hsplit, 2 * C, C, T, 2 * C, EPI_NCHW)
+           // store is contiguous along tokens; bf16 path: fp16 operands.
+           GemmParams p = bf ? gemm(b->w_out, C, b->hcopy, C, C, T, C, EPI_NCHW)
                              : gemm(b->w_out, C, b->h, C, C, T, C, EPI_NCHW);
            p.epi.bias = b->b_out; p.epi.out_act = y; p.epi.resid_act = x;
            p.epi.ntok = N; p.epi.ldo = C;
-           return G(p, ACT_BF16);
+           return G(p, ACT_F16);
          }), "proj_out");
   return ST_OK;
 }

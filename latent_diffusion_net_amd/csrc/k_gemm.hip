@@ -16,9 +16,8 @@
 // the 16 rows of one 16-lane read phase over all 16 bank groups of gfx950's
 // 64-bank LDS.  Rows beyond M or N are clamped on load and masked on store.
 //
-// The residual epilogue can also leave the new fp32 value as two bf16 terms
-// (hi, lo) so that proj_out can take the residual stream at ~16 significant
-// bits through the same bf16 kernel with K doubled.
+// The residual epilogue can also leave the new fp32 value as an fp16 copy,
+// the operand of proj_out (11 significant bits; the output is bf16).
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
@@ -113,12 +112,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       *reinterpret_cast<float4*>(p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = v;
       if constexpr (EPI == EPI_RESID_F32) {
         if (p.epi.out_act) {
-          // h = hi + lo in bf16: hi in columns [0, ldo), lo in [ldo, 2 ldo)
-          const uint32_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
-          bf16_t* hs = static_cast<bf16_t*>(p.epi.out_act) + static_cast<long long>(row) * 2 * p.epi.ldo + C0 + lc;
-          *reinterpret_cast<uint2*>(hs) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-          *reinterpret_cast<uint2*>(hs + p.epi.ldo) =
-              make_uint2(pack2bf(v.x - bf2f(h0), v.y - bf2f(h1)), pack2bf(v.z - bf2f(h2), v.w - bf2f(h3)));
+          // the new h also as fp16 [M][ldo], proj_out's operand
+          f16_t* hc = static_cast<f16_t*>(p.epi.out_act) + static_cast<long long>(row) * p.epi.ldo + C0 + lc;
+          *reinterpret_cast<uint2*>(hc) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
         }
       }
     }

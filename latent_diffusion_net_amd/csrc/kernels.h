@@ -41,8 +41,8 @@ struct EpiParams {
   float* out_f32;         // EPI_STORE_F32 / EPI_RESID_F32
   int ldo;
   void* out_act;          // EPI_GEGLU: [M][F]; EPI_NCHW: y [B][M][ntok];
-                          // EPI_RESID_F32 (optional): the new value as bf16
-                          // hi + lo, [M][2 ldo] (hi in [0, ldo), lo after)
+                          // EPI_RESID_F32 (optional): the new value as fp16
+                          // [M][ldo]
   const void* resid_act;  // EPI_NCHW: x [B][M][ntok]
   int F;                  // EPI_GEGLU: value width
   int ntok;               // EPI_NCHW: tokens per sample
