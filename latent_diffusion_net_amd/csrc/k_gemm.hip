@@ -309,13 +309,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   // split-K: workgroup blockIdx.x takes tile blockIdx.x % tiles and K slice
   // blockIdx.x / tiles (always 0 without split)
-  const int mt = (p.M + TBM - 1) / TBM, nt = (p.N + TBN - 1) / TBN;
+  const int mt = (p.M + TBM - 1) / TBM, nt = (p.N - p.n_off + TBN - 1) / TBN;
   const int kz = blockIdx.x / (mt * nt);
   const int kslice = p.K / (p.ksplit > 1 ? p.ksplit : 1);
   int tm, tn;
   tile_coords(mt, nt, blockIdx.x - kz * mt * nt, tm, tn);
   const int m0 = tm * TBM;
-  const int n0 = tn * TBN;
+  const int n0 = p.n_off + tn * TBN;
   const int M = p.M, N = p.N;
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* Bm = static_cast<const uint16_t*>(p.B);
@@ -374,11 +374,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
 
   const int nk = kslice / BKT;
   uint4 xa[FM], xb[FN], ya[FM], yb[FN];
-  issue(0, sA0, sB0);
-  auto stage = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
-    wait_vmcnt_lds<0>();
-    stage_barrier();
-    if (k + 1 < nk) issue(k + 1, wa, wb);
+  auto steps = [&](const uint16_t* ca, const uint16_t* cb) {
     rd(ca, cb, 0, xa, xb);
     rd(ca, cb, 1, ya, yb);
     mm(xa, xb);
@@ -395,6 +391,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
+  };
+  issue(0, sA0, sB0);
+  auto stage = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
+    wait_vmcnt_lds<0>();
+    stage_barrier();
+    if (k + 1 < nk) issue(k + 1, wa, wb);
+    steps(ca, cb);
   };
   for (int k = 0; k < nk; k += 2) {
     stage(k, sA0, sB0, sA1, sB1);
@@ -499,7 +502,7 @@ namespace {
 template <int WM, int WN, int FM, int FN, int MINB>
 hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStream_t s) {
   constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
-  const dim3 grid(((p.M + TBM - 1) / TBM) * ((p.N + TBN - 1) / TBN) * split);
+  const dim3 grid(((p.M + TBM - 1) / TBM) * ((p.N - p.n_off + TBN - 1) / TBN) * split);
   constexpr int threads = 64 * WM * WN;
 #define ST_PIPE_CASE(E)                                                                          \
   case E:                                                                                        \
@@ -520,8 +523,23 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
 }
 }  // namespace
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.n_off != 0) return hipErrorInvalidValue;
   if (p.K % 64) return hipErrorInvalidValue;
   // the DMA addresses each operand with 32-bit byte offsets
   if (static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL ||
@@ -543,9 +561,25 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   }
   // 256x256 tiles (eight wavefronts of 128x64) when there are enough of
   // them to give most CUs one; otherwise 128x128 tiles, two per CU.
-  const long long big_tiles = static_cast<long long>((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big_tiles >= kBigTileMin) return launch_pipe<2, 4, 4, 2, 1>(p, op, p.epi.kind, 1, s);
-  return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
+  const int mtb = (p.M + 255) / 256, ntb = (p.N + 255) / 256;
+  const long long big_tiles = static_cast<long long>(mtb) * ntb;
+  if (big_tiles < kBigTileMin) return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
+  // When the last round of large tiles would leave more than a quarter of
+  // the CUs idle, the columns of whole rounds take large tiles and the rest
+  // 128x128 tiles (two per CU) in a second launch.
+  const int cus = cu_count();
+  const long long rounds = big_tiles / cus, tail = big_tiles % cus;
+  const int nb = rounds > 0 ? static_cast<int>(rounds * cus / mtb) : 0;
+  if (tail > 0 && 4 * tail < 3LL * cus && nb >= 1 && nb < ntb) {
+    GemmParams q = p;
+    q.N = nb * 256;
+    hipError_t e = launch_pipe<2, 4, 4, 2, 1>(q, op, p.epi.kind, 1, s);
+    if (e != hipSuccess) return e;
+    q.N = p.N;
+    q.n_off = nb * 256;
+    return launch_pipe<2, 2, 2, 2, 2>(q, op, p.epi.kind, 1, s);
+  }
+  return launch_pipe<2, 4, 4, 2, 1>(p, op, p.epi.kind, 1, s);
 }
 
 hipError_t gemm_f32(const GemmParams& p, hipStream_t s) {

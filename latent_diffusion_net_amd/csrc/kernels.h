@@ -62,6 +62,9 @@ struct GemmParams {
   // the slices in order and applies the epilogue element by element.
   int ksplit;
   float* ws;
+  // First output column this launch computes (set by gemm_mfma when it
+  // splits a product's columns between two tile shapes; callers leave 0).
+  int n_off;
 };
 
 // MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
