@@ -434,50 +434,62 @@ __global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(Att
 // Second pass of the key split: for each split query tile, the pieces'
 // partial results are merged in piece order (bitwise reproducible):
 // O = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_i m_i) (the
-// references m_i are base-2 exponents).
-// Two threads per query row, 32 dims each.
+// references m_i are base-2 exponents).  Eight threads per query row, 8
+// dims each, 32 rows per workgroup; every piece's loads are issued before
+// the first sum.
+constexpr int kMaxPieces = 8;  // attention_bf16_plan splits a tile at most 8 ways
 template <int QT>
-__global__ __launch_bounds__(2 * QT) void attn_merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int PF = QT * 66;
-  const int j = blockIdx.x;  // split tile index
+  constexpr int kBlocksPerTile = QT / 32;
+  const int j = blockIdx.x / kBlocksPerTile;  // split tile index
+  const int row = (blockIdx.x - j * kBlocksPerTile) * 32 + (threadIdx.x >> 3);
+  const int g = threadIdx.x & 7;  // dims 8g .. 8g+7
   const int tile = p.n_full + j;
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
   const int qtiles = (p.Nq + QT - 1) / QT;
   const int bh = tile / qtiles;
   const int qrow = (tile - bh * qtiles) * QT + row;
   if (qrow >= p.Nq) return;
   const int b = bh / p.heads, head = bh - b * p.heads;
   const float* tp = p.part + static_cast<long long>(j) * p.nsplit * PF;
+  float m[kMaxPieces], l[kMaxPieces];
+  float4 v[kMaxPieces][2];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    if (i < p.nsplit) {
+      const float* pi = tp + i * PF;
+      m[i] = pi[QT * 64 + row];
+      l[i] = pi[QT * 65 + row];
+      const float4* src = reinterpret_cast<const float4*>(pi + row * 64 + 8 * g);
+      v[i][0] = src[0];
+      v[i][1] = src[1];
+    }
+  }
   float mmax = -INFINITY;
-  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, tp[i * PF + QT * 64 + row]);
-  float acc[32];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) acc[d] = 0.f;
+  for (int i = 0; i < kMaxPieces; ++i)
+    if (i < p.nsplit) mmax = fmaxf(mmax, m[i]);
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
   float den = 0.f;
-  for (int i = 0; i < p.nsplit; ++i) {
-    const float* pi = tp + i * PF;
-    const float w = __builtin_amdgcn_exp2f(pi[QT * 64 + row] - mmax);
-    den += pi[QT * 65 + row] * w;
-    const float4* src = reinterpret_cast<const float4*>(pi + row * 64 + half * 32);
 #pragma unroll
-    for (int d4 = 0; d4 < 8; ++d4) {
-      const float4 v = src[d4];
-      acc[4 * d4] += v.x * w;
-      acc[4 * d4 + 1] += v.y * w;
-      acc[4 * d4 + 2] += v.z * w;
-      acc[4 * d4 + 3] += v.w * w;
+  for (int i = 0; i < kMaxPieces; ++i) {
+    if (i < p.nsplit) {
+      const float w = __builtin_amdgcn_exp2f(m[i] - mmax);
+      den += l[i] * w;
+      acc[0] += v[i][0].x * w; acc[1] += v[i][0].y * w;
+      acc[2] += v[i][0].z * w; acc[3] += v[i][0].w * w;
+      acc[4] += v[i][1].x * w; acc[5] += v[i][1].y * w;
+      acc[6] += v[i][1].z * w; acc[7] += v[i][1].w * w;
     }
   }
   const float inv = 1.0f / den;
   uint16_t* orow = static_cast<uint16_t*>(p.o) +
-                   (static_cast<long long>(b) * p.Nq + qrow) * p.C + head * 64 + half * 32;
-#pragma unroll
-  for (int d8 = 0; d8 < 4; ++d8)
-    *reinterpret_cast<uint4*>(orow + 8 * d8) =
-        make_uint4(pack2bf(acc[8 * d8] * inv, acc[8 * d8 + 1] * inv),
-                   pack2bf(acc[8 * d8 + 2] * inv, acc[8 * d8 + 3] * inv),
-                   pack2bf(acc[8 * d8 + 4] * inv, acc[8 * d8 + 5] * inv),
-                   pack2bf(acc[8 * d8 + 6] * inv, acc[8 * d8 + 7] * inv));
+                   (static_cast<long long>(b) * p.Nq + qrow) * p.C + head * 64 + 8 * g;
+  *reinterpret_cast<uint4*>(orow) =
+      make_uint4(pack2bf(acc[0] * inv, acc[1] * inv), pack2bf(acc[2] * inv, acc[3] * inv),
+                 pack2bf(acc[4] * inv, acc[5] * inv), pack2bf(acc[6] * inv, acc[7] * inv));
 }
 
 #ifndef ST_ATTN_QB
@@ -583,7 +595,8 @@ hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
     attn_bf16_kernel<0, kQB, kNW><<<grid, 64 * kNW, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit <= 1) return e;
-  attn_merge_kernel<kQT><<<tiles - p.n_full, 2 * kQT, 0, s>>>(p);
+  if (p.nsplit > kMaxPieces) return hipErrorInvalidValue;
+  attn_merge_kernel<kQT><<<(tiles - p.n_full) * (kQT / 32), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
