@@ -53,9 +53,10 @@ def block_flops(cfg) -> float:
 # Algorithmic work per launch of each timed kernel kind, and the roofline
 # that bounds it: (row(s) of the method, bound, work per launch).  Flops count
 # 2 per multiply-add; bytes count what the step must read and write at least
-# once (bf16 storage).  proj_in's time also holds the GroupNorm apply, and
-# proj_out is charged its algorithmic 2*T*C^2 (the bf16 path runs it with K
-# doubled: h enters as two bf16 terms).
+# once (bf16 storage).  proj_in's time also holds the GroupNorm apply.  On
+# the bf16 path the LayerNorms have no launch of their own (statistics in the
+# epilogues of the GEMMs that write h, normalisation folded into Q/K/V,
+# cross Q and FF1), so their row is absent and their cost sits in those rows.
 def row_work(cfg):
     T, C, B, N, D, F, h = cfg.T, cfg.C, cfg.B, cfg.N, cfg.D_ctx, cfg.F, cfg.heads
     return {
@@ -90,8 +91,14 @@ def copy_ceiling_gbs(torch, dev):
     return 2.0 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
+LAYERNORM_FOLDED = ("no launch of its own: per-row sums in the epilogues of the GEMMs that "
+                    "write h, normalisation folded into Q/K/V, cross-attention Q and FF1")
+
+
 def row_rates(cfg, timing, copy_gbs):
     rows = {}
+    if getattr(cfg, "dtype", "bf16") == "bf16" and not (timing.get("layernorm") or {}).get("launches"):
+        rows["A3/A7/A12 LayerNorm"] = {"fused": LAYERNORM_FOLDED}
     for kind, (name, bound, work) in row_work(cfg).items():
         t = timing.get(kind)
         if not t or not t["launches"]:

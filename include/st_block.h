@@ -150,7 +150,9 @@ const char *st_last_error(void);
 typedef enum {
   ST_K_GN_STATS = 0, /* GroupNorm statistics */
   ST_K_PROJ_IN,      /* GroupNorm apply + NCHW->tokens + proj_in GEMM */
-  ST_K_LAYERNORM,    /* the three LayerNorms of each layer */
+  ST_K_LAYERNORM,    /* the three LayerNorms of each layer (fp32 storage
+                        only: with bf16 storage they are folded into the
+                        GEMMs around them and have no launch) */
   ST_K_QKV,          /* fused Q/K/V projection of the self-attention */
   ST_K_SELF_ATTN,    /* self-attention over the H*W tokens */
   ST_K_ATTN_OUT,     /* output projections of both attentions (+ residual) */

@@ -8,18 +8,22 @@
 //   proj_in GEMM                    u, W_in               -> h [T][C] fp32
 //   context K/V GEMM (all layers)   ctx, [Wk2;Wv2]*depth  -> Kc, Vc^T per layer
 //   per layer:
-//     LayerNorm 1                   h                     -> u
-//     Q/K/V GEMM                    u, [Wq1;Wk1;Wv1]      -> Q, K, V^T (per head)
+//     Q/K/V GEMM, LayerNorm 1 folded  h16, [Wq1;Wk1;Wv1]*g1 -> Q, K, V^T (per head)
 //     self-attention                Q, K, V^T             -> O [T][C] bf16
 //     out-projection GEMM           O, Wo1                -> h += .
-//     LayerNorm 2, cross Q GEMM     h, Wq2                -> Q
+//     cross Q GEMM, LayerNorm 2 folded  h16, Wq2*g2       -> Q
 //     cross-attention               Q, Kc, Vc^T           -> O
 //     out-projection GEMM           O, Wo2                -> h += .
-//     LayerNorm 3, FF1 GEMM+GEGLU   h, W1 (repacked)      -> f [T][F] bf16
+//     FF1 GEMM+GEGLU, LayerNorm 3 folded  h16, W1*g3      -> f [T][F] fp16
 //     FF2 GEMM                      f, W2                 -> h += .
-//   proj_out GEMM, transposed       W_out, h (fp16 copy)  -> y = NCHW(.) + x
-//     (the last FF2 also writes h as fp16, [T][C])
-// The fp32 debug path runs the same schedule with fp32 buffers and kernels,
+//   proj_out GEMM, transposed       W_out, h16            -> y = NCHW(.) + x
+// Every GEMM that writes h (proj_in and the three residual products) also
+// writes h16, its fp16 copy, and per row and 64 channels the sum and the sum
+// of squared deviations of h; a product behind a LayerNorm reads h16 with
+// gamma folded into its weights and beta into its bias, and corrects each
+// output by the row's mean and 1/std combined from those sums:
+//   LN(h) W^T = rstd * (h (W*gamma)^T - mean * rowsum(W*gamma)) + W beta.
+// The fp32 debug path runs LayerNorm as its own pass on fp32 buffers, and
 // GEGLU as its own pass.
 #include <hip/hip_runtime.h>
 
@@ -59,6 +63,10 @@ inline long long round_up(long long v, long long m) { return (v + m - 1) / m * m
 struct LayerDev {
   float* ln_w[3];
   float* ln_b[3];
+  // bf16 path: LayerNorm i is folded into the product that follows it (Q/K/V,
+  // cross Q, FF1): those weights hold W * gamma in fp16, their biases gain
+  // W beta, and ln_g[i] holds the row sums of the folded weights.
+  float* ln_g[3];
   void* wqkv;  // [3C][C]: Wq1, Wk1, Wv1
   float* bqkv;
   void* wo1;
@@ -102,7 +110,8 @@ struct st_block {
   int gn_max_split;
   void* u;
   float* h;
-  void* hcopy;  // bf16 path: [T][C] fp16 copy of the last h, proj_out's operand
+  void* hcopy;  // bf16 path: [T][C] fp16 copy of h, operand of the next product
+  float2* hstats;  // bf16 path: [T][C/64] sums and squared deviations of h
   void *q, *k, *vt, *o, *f;
   float* z;  // fp32 path: FF1 output before GEGLU
   void *kc, *vct;
@@ -188,6 +197,15 @@ struct Creator {
   int* overflow = nullptr;
   void to_f16(void* d, long long n, const char* what) {
     if (ok() && b->bf16 && d) dev(bf16_to_f16_inplace(d, n, overflow, s), what);
+  }
+  // bf16 path: LayerNorm (gamma, beta) folded into the rows x C weights w
+  // that follow it (fp16 on return), their bias and the row sums *g.
+  void fold_ln(void* w, int rows, int cols, const float* gamma, const float* beta,
+               float* bias, const int* map, float*& g, const char* what) {
+    g = nullptr;
+    if (!ok() || !b->bf16) return;
+    g = static_cast<float*>(alloc(sizeof(float) * rows, what));
+    if (ok()) dev(weight_fold_layernorm(w, rows, cols, gamma, beta, bias, map, g, overflow, s), what);
   }
 };
 
@@ -310,7 +328,6 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
       cr.copy(d.wqkv, lw.q1_w, CC * es, "q1_w");
       cr.copy(static_cast<char*>(d.wqkv) + CC * es, lw.k1_w, CC * es, "k1_w");
       cr.copy(static_cast<char*>(d.wqkv) + 2 * CC * es, lw.v1_w, CC * es, "v1_w");
-      cr.to_f16(d.wqkv, 3 * CC, "Q/K/V weights to fp16");
     }
     d.bqkv = static_cast<float*>(cr.alloc(3LL * C * sizeof(float), "Q/K/V biases"));
     if (d.bqkv) {
@@ -318,11 +335,12 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
       cr.vec_into(d.bqkv + C, lw.k1_b, C, 0.f, "k1_b");
       cr.vec_into(d.bqkv + 2 * C, lw.v1_b, C, 0.f, "v1_b");
     }
+    cr.fold_ln(d.wqkv, 3 * C, C, d.ln_w[0], d.ln_b[0], d.bqkv, nullptr, d.ln_g[0], "fold LayerNorm 1");
     d.wo1 = cr.mat(lw.o1_w, C, C, "o1_w");
     d.bo1 = cr.vec(lw.o1_b, C, 0.f, "o1_b");
     d.wq2 = cr.mat(lw.q2_w, C, C, "q2_w");
-    cr.to_f16(d.wq2, CC, "q2_w to fp16");
     d.bq2 = cr.vec(lw.q2_b, C, 0.f, "q2_b");
+    cr.fold_ln(d.wq2, C, C, d.ln_w[1], d.ln_b[1], d.bq2, nullptr, d.ln_g[1], "fold LayerNorm 2");
     d.wo2 = cr.mat(lw.o2_w, C, C, "o2_w");
     d.bo2 = cr.vec(lw.o2_b, C, 0.f, "o2_b");
     if (b->wkv && b->bkv) {
@@ -339,9 +357,10 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
         cr.dev(gather_rows(lw.ff1_w, d.w1, d_map, 2 * F, static_cast<long long>(C) * es, s), "ff1_w repack");
       else
         cr.copy(d.w1, lw.ff1_w, 2LL * F * C * es, "ff1_w");
-      cr.to_f16(d.w1, 2LL * F * C, "ff1_w to fp16");
     }
     d.b1 = cr.vec(lw.ff1_b, 2LL * F, 0.f, "ff1_b");
+    // rows repacked, biases in the original order
+    cr.fold_ln(d.w1, 2 * F, C, d.ln_w[2], d.ln_b[2], d.b1, d_map, d.ln_g[2], "fold LayerNorm 3");
     d.w2 = cr.mat(lw.ff2_w, C, F, "ff2_w");
     cr.to_f16(d.w2, static_cast<long long>(C) * F, "ff2_w to fp16");
     d.b2 = cr.vec(lw.ff2_b, C, 0.f, "ff2_b");
@@ -353,6 +372,9 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->u = cr.alloc(T * C * es, "normalised activations");
   b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
   b->hcopy = b->bf16 ? cr.alloc(T * static_cast<long long>(C) * es, "fp16 residual stream") : nullptr;
+  b->hstats = b->bf16 ? static_cast<float2*>(cr.alloc(T * static_cast<long long>(C / 64) * sizeof(float2),
+                                                      "residual stream statistics"))
+                      : nullptr;
   const long long headbuf = static_cast<long long>(B) * heads * b->npad * 64 * es;
   b->q = cr.alloc(headbuf, "Q");
   b->k = cr.alloc(headbuf, "K");
@@ -465,6 +487,9 @@ hipError_t run(st_block* b, int kind, hipStream_t s, Fn&& launch) {
   return r;
 }
 
+// LayerNorm's epsilon (the default of the pages' Transformer blocks).
+constexpr float kLayerNormEps = 1e-5f;
+
 GemmParams gemm(const void* A, long long lda, const void* Bm, long long ldb,
                 int M, int N, int K, int kind) {
   GemmParams p{};
@@ -491,6 +516,18 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   auto G = [&](const GemmParams& p, int op) {
     return bf ? gemm_mfma(p, op, s) : gemm_f32(p, s);
   };
+  // bf16 path: every product that writes h also leaves it as fp16 with its
+  // per-row statistics, and the products behind a LayerNorm read that copy
+  // with the norm folded into their weights (no LayerNorm launch).
+  auto keep_h = [&](GemmParams& p) {
+    if (bf) { p.epi.out_act = b->hcopy; p.epi.row_stats = b->hstats; }
+  };
+  auto normed = [&](GemmParams& p, const LayerDev& L, int i) {
+    if (!bf) return;
+    p.A = b->hcopy;
+    p.epi.ln_stats = b->hstats; p.epi.ln_g = L.ln_g[i];
+    p.epi.ln_blocks = C / 64; p.epi.ln_eps = kLayerNormEps;
+  };
 
   ST_TRY(run(b, ST_K_GN_STATS, s, [&] {
            return gn_stats(x, bf, B, C, N, b->gn_part, b->gn_max_split, s);
@@ -501,6 +538,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
            if (e != hipSuccess) return e;
            GemmParams p = gemm(b->u, C, b->w_in, C, T, C, C, EPI_STORE_F32);
            p.epi.bias = b->b_in; p.epi.out_f32 = b->h; p.epi.ldo = C;
+           keep_h(p);
            return G(p, ACT_F16);
          }), "proj_in");
   int stage = 0;
@@ -526,11 +564,13 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   for (int l = 0; l < b->depth; ++l) {
     const LayerDev& L = b->L[l];
     // ---- self-attention sublayer
-    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
-             return layernorm(b->h, L.ln_w[0], L.ln_b[0], b->u, act, T, C, s);
-           }), "LayerNorm 1");
+    if (!bf)
+      ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+               return layernorm(b->h, L.ln_w[0], L.ln_b[0], b->u, act, T, C, s);
+             }), "LayerNorm 1");
     ST_TRY(run(b, ST_K_QKV, s, [&] {
              GemmParams p = gemm(b->u, C, L.wqkv, C, T, 3 * C, C, EPI_HEADS);
+             normed(p, L, 0);
              p.epi.bias = L.bqkv;
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = b->k; p.epi.hs.dst[2] = b->vt;
              if (bf) p.epi.hs.scale[0] = attention_bf16_q_scale();
@@ -551,16 +591,19 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
              GemmParams p = gemm(b->o, C, L.wo1, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo1; p.epi.out_f32 = b->h; p.epi.ldo = C;
+             keep_h(p);
              return G(p, ACT_BF16);
            }), "self-attention out-projection");
     ++stage;
     if (dump()) break;
     // ---- cross-attention sublayer
-    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
-             return layernorm(b->h, L.ln_w[1], L.ln_b[1], b->u, act, T, C, s);
-           }), "LayerNorm 2");
+    if (!bf)
+      ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+               return layernorm(b->h, L.ln_w[1], L.ln_b[1], b->u, act, T, C, s);
+             }), "LayerNorm 2");
     ST_TRY(run(b, ST_K_CROSS_Q, s, [&] {
              GemmParams p = gemm(b->u, C, L.wq2, C, T, C, C, EPI_HEADS);
+             normed(p, L, 1);
              p.epi.bias = L.bq2;
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = nullptr; p.epi.hs.dst[2] = nullptr;
              if (bf) p.epi.hs.scale[0] = attention_bf16_q_scale();
@@ -582,17 +625,20 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
              GemmParams p = gemm(b->o, C, L.wo2, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo2; p.epi.out_f32 = b->h; p.epi.ldo = C;
+             keep_h(p);
              return G(p, ACT_BF16);
            }), "cross-attention out-projection");
     ++stage;
     if (dump()) break;
     // ---- feed-forward sublayer
-    ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
-             return layernorm(b->h, L.ln_w[2], L.ln_b[2], b->u, act, T, C, s);
-           }), "LayerNorm 3");
+    if (!bf)
+      ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
+               return layernorm(b->h, L.ln_w[2], L.ln_b[2], b->u, act, T, C, s);
+             }), "LayerNorm 3");
     ST_TRY(run(b, ST_K_FF1_GEGLU, s, [&] {
              if (bf) {
                GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_GEGLU);
+               normed(p, L, 2);
                p.epi.bias = L.b1; p.epi.out_act = b->f; p.epi.F = F;
                return gemm_mfma(p, ACT_F16, s);
              }
@@ -605,8 +651,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     ST_TRY(run(b, ST_K_FF2, s, [&] {
              GemmParams p = gemm(b->f, F, L.w2, F, T, C, F, EPI_RESID_F32);
              p.epi.bias = L.b2; p.epi.out_f32 = b->h; p.epi.ldo = C;
-             // the last layer also leaves h as fp16 for proj_out
-             if (bf && l + 1 == b->depth && stop_stage < 0) p.epi.out_act = b->hcopy;
+             keep_h(p);
              return G(p, ACT_F16);
            }), "feed-forward 2");
     ++stage;

@@ -21,6 +21,8 @@
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
+#include <type_traits>
+
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
@@ -64,11 +66,32 @@ __device__ __forceinline__ int stg(int row, int col) {
   return row * 64 + (col ^ (((row >> 2) & 1) << 5));
 }
 
-template <int EPI>
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xF>(v);  // row_mirror
+  return v;
+}
+
+// rstd * a - mean * rstd * g for four columns of one row (k = (rstd, mean * rstd)).
+__device__ __forceinline__ float4 ln_fix(float4 a, float2 k, float4 g) {
+  return make_float4(fmaf(a.x, k.x, -k.y * g.x), fmaf(a.y, k.x, -k.y * g.y),
+                     fmaf(a.z, k.x, -k.y * g.z), fmaf(a.w, k.x, -k.y * g.w));
+}
+
+// Folded LayerNorm (LN: EPI_HEADS and EPI_GEGLU only):
+// ln_rows (LDS) holds (rstd, mean * rstd) for the 64 rows of this block and
+// ln_cols (LDS) the folded weights' sums for its 64 columns; each value read
+// back from the staging tile becomes rstd * acc - mean * rstd * g.
+template <int EPI, bool LN>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
                                              const floatx16 (&acc)[2][2],
                                              int m0, int n0, int wm, int wn,
-                                             int lane, float* stage) {
+                                             int lane, float* stage,
+                                             const float2* ln_rows, const float* ln_cols) {
+  static_assert(!LN || EPI == EPI_HEADS || EPI == EPI_GEGLU, "folded LayerNorm kinds");
   const int l32 = lane & 31, lhi = lane >> 5;
   const int M = p.M, N = p.N;
   const int R0 = m0 + wm * 64, C0 = n0 + wn * 64;
@@ -110,12 +133,20 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         v.x += hin[it].x; v.y += hin[it].y; v.z += hin[it].z; v.w += hin[it].w;
       }
       *reinterpret_cast<float4*>(p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = v;
-      if constexpr (EPI == EPI_RESID_F32) {
-        if (p.epi.out_act) {
-          // the new h also as fp16 [M][ldo], proj_out's operand
-          f16_t* hc = static_cast<f16_t*>(p.epi.out_act) + static_cast<long long>(row) * p.epi.ldo + C0 + lc;
-          *reinterpret_cast<uint2*>(hc) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
-        }
+      if (p.epi.out_act) {
+        // the new values also as fp16 [M][ldo] (the operand of the next
+        // product)
+        f16_t* hc = static_cast<f16_t*>(p.epi.out_act) + static_cast<long long>(row) * p.epi.ldo + C0 + lc;
+        *reinterpret_cast<uint2*>(hc) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
+      }
+      if (p.epi.row_stats) {
+        // the row's 64 values sit in the 16 lanes of one DPP row
+        const float sum = row16_sum((v.x + v.y) + (v.z + v.w));
+        const float mb = sum * (1.0f / 64.0f);
+        const float dx = v.x - mb, dy = v.y - mb, dz = v.z - mb, dw = v.w - mb;
+        const float m2 = row16_sum((dx * dx + dy * dy) + (dz * dz + dw * dw));
+        if ((lane & 15) == 0)
+          p.epi.row_stats[static_cast<long long>(row) * (p.epi.ldo >> 6) + (C0 >> 6)] = make_float2(sum, m2);
       }
     }
   } else if constexpr (EPI == EPI_GEGLU) {
@@ -131,13 +162,23 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       bg[k] = p.epi.bias ? p.epi.bias[F + fc0 + lc + k] : 0.f;
     }
     f16_t* out = static_cast<f16_t*>(p.epi.out_act);
+    float4 lgv = make_float4(0.f, 0.f, 0.f, 0.f), lgg = lgv;
+    if constexpr (LN) {
+      lgv = *reinterpret_cast<const float4*>(ln_cols + lc);
+      lgg = *reinterpret_cast<const float4*>(ln_cols + 32 + lc);
+    }
 #pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int lr = it * 8 + (lane >> 3);
       const int row = R0 + lr;
       if (row >= M) break;
-      const float4 v = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
-      const float4 g = *reinterpret_cast<const float4*>(&stage[stg(lr, 32 + lc)]);
+      float4 v = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+      float4 g = *reinterpret_cast<const float4*>(&stage[stg(lr, 32 + lc)]);
+      if constexpr (LN) {
+        const float2 k = ln_rows[lr];
+        v = ln_fix(v, k, lgv);
+        g = ln_fix(g, k, lgg);
+      }
       const uint2 pk = make_uint2(
           pack2h((v.x + bv[0]) * gelu_as(g.x + bg[0]), (v.y + bv[1]) * gelu_as(g.y + bg[1])),
           pack2h((v.z + bv[2]) * gelu_as(g.z + bg[2]), (v.w + bv[3]) * gelu_as(g.w + bg[3])));
@@ -160,6 +201,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       float bb[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) bb[k] = bias ? bias[lc + k] : 0.f;
+      float4 lg = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (LN) lg = *reinterpret_cast<const float4*>(ln_cols + lc);
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
         const int lr = it * 4 + (lane >> 4);
@@ -167,7 +210,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         if (row >= M) break;
         const int b = row / hs.rows_per_batch;
         const int n = row - b * hs.rows_per_batch;
-        const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+        float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+        if constexpr (LN) c = ln_fix(c, ln_rows[lr], lg);
         const uint2 pk = make_uint2(pack2bf((c.x + bb[0]) * sc, (c.y + bb[1]) * sc),
                                     pack2bf((c.z + bb[2]) * sc, (c.w + bb[3]) * sc));
         const long long bh = static_cast<long long>(b) * hs.heads + head;
@@ -177,6 +221,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       // V^T [bh][64][npad]: lane -> one dim, 4 consecutive tokens
       const int dim = lane;
       const float bb = bias ? bias[dim] : 0.f;
+      float lg = 0.f;
+      if constexpr (LN) lg = ln_cols[dim];
       const bool vec = (hs.rows_per_batch & 3) == 0;
 #pragma unroll 2
       for (int it = 0; it < 16; ++it) {
@@ -185,7 +231,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         if (row0 >= M) break;
         float v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = (stage[stg(lr0 + k, dim)] + bb) * sc;
+        for (int k = 0; k < 4; ++k) {
+          float a = stage[stg(lr0 + k, dim)];
+          if constexpr (LN) {
+            const float2 kk = ln_rows[lr0 + k];
+            a = fmaf(a, kk.x, -kk.y * lg);
+          }
+          v[k] = (a + bb) * sc;
+        }
         if (vec && row0 + 3 < M) {
           const int b = row0 / hs.rows_per_batch;
           const int n = row0 - b * hs.rows_per_batch;
@@ -289,7 +342,7 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, uint16_t* ld
 // other buffers, then the four 16-wide K steps, the LDS operand reads of
 // step s+1 issued before the MFMAs of step s (two register sets; the
 // scheduling groups keep the compiler from folding them back into one).
-template <int EPI, typename OpT, int WM, int WN, int FM, int FN, int MINB>
+template <int EPI, typename OpT, int WM, int WN, int FM, int FN, int MINB, bool LN>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
@@ -304,6 +357,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   __shared__ __attribute__((aligned(16))) uint16_t sA1[TBM * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sB0[TBN * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[TBN * BKT];
+  // folded LayerNorm: (rstd, mean * rstd) per row and g per column
+  __shared__ float2 ln_tab[LN ? TBM : 1];
+  __shared__ __attribute__((aligned(16))) float ln_gtab[LN ? TBN : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
@@ -392,7 +448,67 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * F, 0);
   };
+  // Folded LayerNorm: the folded weights' column sums of the tile, and per
+  // row (rstd, mean * rstd) from the 64-column blocks' sums s_k and squared
+  // deviations d_k, in fp64: mean = sum s_k / K, var = sum (d_k + s_k^2 /
+  // 64) / K - mean^2.  Two threads per row take alternate blocks.  The loads
+  // are issued before the first stage's DMA and used after it, so that no
+  // wait for them also waits for the DMA (the counter is in order).
+  constexpr int kLnRegs = 10;  // blocks per thread held in registers (K <= 1280)
+  float2 lnv[kLnRegs];
+  float ln_gv = 0.f;
+  double ln_sum = 0.0, ln_sq = 0.0, ln_inv_k = 0.0;
+  if constexpr (LN) {
+    static_assert(2 * TBM == 64 * NW && TBN <= 64 * NW, "two threads per row, one per column");
+    const int t = threadIdx.x, half = t & 1;
+    ln_gv = p.epi.ln_g[min(n0 + t % TBN, N - 1)];
+    const float2* st = p.epi.ln_stats + static_cast<long long>(min(m0 + (t >> 1), M - 1)) * p.epi.ln_blocks;
+#pragma unroll
+    for (int i = 0; i < kLnRegs; ++i) lnv[i] = make_float2(0.f, 0.f);
+    auto load = [&](auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
+      static_assert((NB + 1) / 2 <= kLnRegs, "registers");
+      ln_inv_k = 1.0 / (64.0 * NB);
+#pragma unroll
+      for (int i = 0; i < (NB + 1) / 2; ++i) {
+        const float2 x = st[min(2 * i + half, NB - 1)];
+        lnv[i] = (NB % 2 == 0 || 2 * i + half < NB) ? x : make_float2(0.f, 0.f);
+      }
+    };
+    switch (p.epi.ln_blocks) {
+      case 5: load(std::integral_constant<int, 5>{}); break;
+      case 10: load(std::integral_constant<int, 10>{}); break;
+      case 20: load(std::integral_constant<int, 20>{}); break;
+      default:
+        ln_inv_k = 1.0 / (64.0 * p.epi.ln_blocks);
+        for (int kb = half; kb < p.epi.ln_blocks; kb += 2) {
+          const float2 v = st[kb];
+          ln_sum += v.x;
+          ln_sq += static_cast<double>(v.y) + static_cast<double>(v.x) * v.x * (1.0 / 64.0);
+        }
+    }
+  }
   issue(0, sA0, sB0);
+  if constexpr (LN) {
+    // the sums stay below the DMA issue (the empty statements take the
+    // loaded values after it)
+#pragma unroll
+    for (int i = 0; i < kLnRegs; ++i) asm volatile("" : "+v"(lnv[i].x), "+v"(lnv[i].y)::"memory");
+    asm volatile("" : "+v"(ln_gv)::"memory");
+    const int t = threadIdx.x, half = t & 1;
+    ln_gtab[t % TBN] = ln_gv;
+#pragma unroll
+    for (int i = 0; i < kLnRegs; ++i) {
+      ln_sum += lnv[i].x;
+      ln_sq += static_cast<double>(lnv[i].y) + static_cast<double>(lnv[i].x) * lnv[i].x * (1.0 / 64.0);
+    }
+    ln_sum += __shfl_xor(ln_sum, 1, 64);
+    ln_sq += __shfl_xor(ln_sq, 1, 64);
+    const double mean = ln_sum * ln_inv_k;
+    const float var = static_cast<float>(fmax(ln_sq * ln_inv_k - mean * mean, 0.0));
+    const float rstd = rsqrtf(var + p.epi.ln_eps);
+    if (!half) ln_tab[t >> 1] = make_float2(rstd, static_cast<float>(mean) * rstd);
+  }
   auto stage = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
     wait_vmcnt_lds<0>();
     stage_barrier();
@@ -425,6 +541,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     q.epi.bias = nullptr;
     q.epi.out_f32 = p.ws + static_cast<long long>(kz) * M * N;
     q.epi.ldo = N;
+    q.epi.out_act = nullptr;
+    q.epi.row_stats = nullptr;
   }
 #pragma unroll
   for (int si = 0; si < FM / 2; ++si)
@@ -433,8 +551,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
       const floatx16 sub[2][2] = {{acc[2 * si][2 * sj], acc[2 * si][2 * sj + 1]},
                                   {acc[2 * si + 1][2 * sj], acc[2 * si + 1][2 * sj + 1]}};
       const int r0 = m0 + wm * FM * 32 + si * 64, c0 = n0 + wn * FN * 32 + sj * 64;
-      if (p.ksplit > 1) epilogue_lds<EPI_STORE_F32>(q, sub, r0, c0, 0, 0, lane, stg_area);
-      else epilogue_lds<EPI>(p, sub, r0, c0, 0, 0, lane, stg_area);
+      if (p.ksplit > 1)
+        epilogue_lds<EPI_STORE_F32, false>(q, sub, r0, c0, 0, 0, lane, stg_area, nullptr, nullptr);
+      else
+        epilogue_lds<EPI, LN>(p, sub, r0, c0, 0, 0, lane, stg_area, ln_tab + (r0 - m0),
+                              ln_gtab + (c0 - n0));
     }
 }
 
@@ -504,21 +625,24 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
   constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
   const dim3 grid(((p.M + TBM - 1) / TBM) * ((p.N - p.n_off + TBN - 1) / TBN) * split);
   constexpr int threads = 64 * WM * WN;
-#define ST_PIPE_CASE(E)                                                                          \
-  case E:                                                                                        \
-    if (op == ACT_F16) gemm_pipe_kernel<E, f16_t, WM, WN, FM, FN, MINB><<<grid, threads, 0, s>>>(p); \
-    else gemm_pipe_kernel<E, bf16_t, WM, WN, FM, FN, MINB><<<grid, threads, 0, s>>>(p);          \
-    break;
+#define ST_PIPE_LAUNCH(E, LN)                                                                          \
+  if (op == ACT_F16) gemm_pipe_kernel<E, f16_t, WM, WN, FM, FN, MINB, LN><<<grid, threads, 0, s>>>(p); \
+  else gemm_pipe_kernel<E, bf16_t, WM, WN, FM, FN, MINB, LN><<<grid, threads, 0, s>>>(p);
+  const bool ln = p.epi.ln_stats != nullptr;
   switch (kind) {
-    ST_PIPE_CASE(EPI_STORE_F32)
-    ST_PIPE_CASE(EPI_RESID_F32)
-    ST_PIPE_CASE(EPI_HEADS)
-    ST_PIPE_CASE(EPI_GEGLU)
-    ST_PIPE_CASE(EPI_NCHW)
+    case EPI_STORE_F32: ST_PIPE_LAUNCH(EPI_STORE_F32, false) break;
+    case EPI_RESID_F32: ST_PIPE_LAUNCH(EPI_RESID_F32, false) break;
+    case EPI_NCHW: ST_PIPE_LAUNCH(EPI_NCHW, false) break;
+    case EPI_HEADS:
+      if (ln) { ST_PIPE_LAUNCH(EPI_HEADS, true) } else { ST_PIPE_LAUNCH(EPI_HEADS, false) }
+      break;
+    case EPI_GEGLU:
+      if (ln) { ST_PIPE_LAUNCH(EPI_GEGLU, true) } else { ST_PIPE_LAUNCH(EPI_GEGLU, false) }
+      break;
     default:
       return hipErrorInvalidValue;
   }
-#undef ST_PIPE_CASE
+#undef ST_PIPE_LAUNCH
   return hipGetLastError();
 }
 }  // namespace
@@ -540,6 +664,12 @@ static int cu_count() {
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.n_off != 0) return hipErrorInvalidValue;
+  if (p.epi.ln_stats && (!p.epi.ln_g || p.epi.ln_blocks * 64 != p.K ||
+                         (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_GEGLU)))
+    return hipErrorInvalidValue;
+  if (p.epi.row_stats && (p.epi.ldo % 64 || p.N % 64 ||
+                          (p.epi.kind != EPI_STORE_F32 && p.epi.kind != EPI_RESID_F32)))
+    return hipErrorInvalidValue;
   if (p.K % 64) return hipErrorInvalidValue;
   // the DMA addresses each operand with 32-bit byte offsets
   if (static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL ||
@@ -547,7 +677,7 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
     return hipErrorInvalidValue;
   const int split = p.ksplit > 1 ? p.ksplit : 1;
   if (split > 1) {
-    if (!p.ws || p.K % (split * 64) || op != ACT_BF16 ||
+    if (!p.ws || p.K % (split * 64) || op != ACT_BF16 || p.epi.ln_stats || p.epi.row_stats ||
         (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))
       return hipErrorInvalidValue;
     // the slices (the kernel switches to the plain fp32 store), then the sum
@@ -584,6 +714,7 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
 
 hipError_t gemm_f32(const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.epi.ln_stats || p.epi.row_stats || p.n_off) return hipErrorInvalidValue;
   dim3 grid((p.N + FT - 1) / FT, (p.M + FT - 1) / FT);
   switch (p.epi.kind) {
     case EPI_STORE_F32: gemm_f32_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(p); break;

@@ -368,6 +368,46 @@ hipError_t bf16_to_f16_inplace(void* buf, long long n, int* overflow,
   return hipGetLastError();
 }
 
+// One wavefront per weight row: the row's elements strided over the lanes,
+// fp64 sums reduced across the wavefront.
+__global__ __launch_bounds__(64) void weight_fold_layernorm_kernel(
+    uint16_t* __restrict__ w, int C, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ bias,
+    const int* __restrict__ map, float* __restrict__ g, int* __restrict__ overflow) {
+  const int j = blockIdx.x;
+  uint16_t* row = w + static_cast<long long>(j) * C;
+  double gs = 0.0, bs = 0.0;
+  bool big = false;
+  for (int c = threadIdx.x; c < C; c += 64) {
+    const float v = bf2f(row[c]);
+    const f16_t h = static_cast<f16_t>(v * gamma[c]);
+    big |= fabsf(v * gamma[c]) > 65504.0f;
+    row[c] = __builtin_bit_cast(uint16_t, h);
+    gs += static_cast<double>(static_cast<float>(h));
+    bs += static_cast<double>(beta[c]) * static_cast<double>(v);
+  }
+  if (big) *overflow = 1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    gs += __shfl_xor(gs, o, 64);
+    bs += __shfl_xor(bs, o, 64);
+  }
+  if (threadIdx.x == 0) {
+    g[j] = static_cast<float>(gs);
+    const int bj = map ? map[j] : j;
+    bias[bj] = static_cast<float>(static_cast<double>(bias[bj]) + bs);
+  }
+}
+
+hipError_t weight_fold_layernorm(void* w, int rows, int C, const float* gamma,
+                                 const float* beta, float* bias, const int* map,
+                                 float* g, int* overflow, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  weight_fold_layernorm_kernel<<<rows, 64, 0, s>>>(static_cast<uint16_t*>(w), C, gamma, beta,
+                                                   bias, map, g, overflow);
+  return hipGetLastError();
+}
+
 __global__ void gather_rows_kernel(const uint4* __restrict__ src,
                                    uint4* __restrict__ dst,
                                    const int* __restrict__ map,

@@ -47,6 +47,19 @@ struct EpiParams {
   int F;                  // EPI_GEGLU: value width
   int ntok;               // EPI_NCHW: tokens per sample
   HeadSplit hs;
+  // EPI_STORE_F32 / EPI_RESID_F32 (optional): per row and 64-column block of
+  // the new values, their sum and their sum of squared deviations from the
+  // block's mean, [M][ldo / 64].
+  float2* row_stats;
+  // LayerNorm folded into the product (EPI_HEADS or EPI_GEGLU, no split-K):
+  // A holds h and B the weights times gamma (weight_fold_layernorm), and each
+  // product is corrected per row to rstd * (acc - mean * ln_g[col]) before
+  // the epilogue, with mean and rstd = 1 / sqrt(var + ln_eps) of the row of
+  // h combined from ln_stats (written as row_stats above; K = 64 * ln_blocks).
+  const float2* ln_stats;
+  const float* ln_g;
+  int ln_blocks;
+  float ln_eps;
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T, then the epilogue.
@@ -132,6 +145,14 @@ hipError_t to_f32(const void* src, bool bf16, float* dst, long long n,
 // above 65504 set *overflow to 1).
 hipError_t bf16_to_f16_inplace(void* buf, long long n, int* overflow,
                                hipStream_t s);
+// LayerNorm folded into the Linear layer that follows it, for rows x C
+// weights w (bf16 on entry, fp16 on return, in place): w[j][c] <- w[j][c] *
+// gamma[c] rounded to fp16, g[j] = sum_c of the rounded w[j][c], and
+// bias[map ? map[j] : j] += sum_c beta[c] * w[j][c] (the entry weights);
+// sums in fp64.  Magnitudes above 65504 set *overflow to 1.
+hipError_t weight_fold_layernorm(void* w, int rows, int C, const float* gamma,
+                                 const float* beta, float* bias, const int* map,
+                                 float* g, int* overflow, hipStream_t s);
 // dst row r = src row map[r], rows of `row_bytes` bytes (multiple of 16).
 hipError_t gather_rows(const void* src, void* dst, const int* map, int rows,
                        long long row_bytes, hipStream_t s);

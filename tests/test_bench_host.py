@@ -116,3 +116,6 @@ def test_row_rates_units(bench):
     assert ln["unit"] == "GB/s" and abs(ln["achieved"] - cfg.T * cfg.C * 6 / 6e-6 / 1e9) < 0.1
     assert abs(ln["frac_of_copy"] - ln["achieved"] / 5000.0) < 1e-3
     assert "A4 Q/K/V projection" not in r  # no launches: no row
+    # bf16 path without LayerNorm launches: the row says where the work went
+    r2 = bench.row_rates(cfg, {"self_attn": {"ms": 0.2, "launches": 2}}, 5000.0)
+    assert r2["A3/A7/A12 LayerNorm"] == {"fused": bench.LAYERNORM_FOLDED}
