@@ -97,21 +97,21 @@ __device__ __forceinline__ float gelu_erf(float g) {
 }
 
 // The same GELU with erf from Abramowitz & Stegun, Handbook of Mathematical
-// Functions, formula 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 +
-// t a5)))) exp(-x^2), t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7; odd in
-// x.  Used where the result is rounded to a 16-bit type, whose rounding
-// (>= 2^-12 relative) is far larger than that error.
+// Functions, formula 7.1.26: erf(x) = 1 - P(t) exp(-x^2), P(t) = t (a1 + t
+// (a2 + t (a3 + t (a4 + t a5)))), t = 1 / (1 + p x), x >= 0, |error| <=
+// 1.5e-7; erf is odd.  With x = |g| / sqrt 2, g erf(g / sqrt 2) = |g| (1 - P
+// exp(-g^2 / 2)), so GELU(g) = max(g, 0) - |g| / 2 * P * exp(-g^2 / 2).
+// Used where the result is rounded to a 16-bit type, whose rounding (>=
+// 2^-12 relative) is far larger than that error.
 __device__ __forceinline__ float gelu_as(float g) {
-  const float x = fabsf(g) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float a = fabsf(g);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2316418882663604f, a, 1.0f));  // p / sqrt 2
   float poly = fmaf(t, 1.061405429f, -1.453152027f);
   poly = fmaf(t, poly, 1.421413741f);
   poly = fmaf(t, poly, -0.284496736f);
   poly = fmaf(t, poly, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
-  const float erf_abs = fmaf(-poly, e, 1.0f);
-  return 0.5f * g * (1.0f + copysignf(erf_abs, g));
+  const float e = __builtin_amdgcn_exp2f(g * g * -0.7213475204444817f);  // exp(-g^2 / 2)
+  return fmaf(-0.5f * a, poly * t * e, fmaxf(g, 0.0f));
 }
 
 // 32x32x16 MFMA with fp32 accumulation, bf16 or fp16 operands (8 per lane).
