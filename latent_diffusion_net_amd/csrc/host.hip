@@ -17,14 +17,15 @@
 //     FF1 GEMM+GEGLU, LayerNorm 3 folded  h16, W1*g3      -> f [T][F] fp16
 //     FF2 GEMM                      f, W2                 -> h += .
 //   proj_out GEMM, transposed       W_out, h16            -> y = NCHW(.) + x
-// Every GEMM that writes h (proj_in and the three residual products) also
-// writes h16, its fp16 copy, and per row and 64 channels the sum and the sum
-// of squared deviations of h; a product behind a LayerNorm reads h16 with
-// gamma folded into its weights and beta into its bias, and corrects each
-// output by the row's mean and 1/std combined from those sums:
+// The residual stream h lives in fp16 (h16).  Every GEMM that writes it
+// (proj_in and the three residual products) also writes, per row and 64
+// channels, the sum and the sum of squared deviations of the stored values;
+// a product behind a LayerNorm reads h16 with gamma folded into its weights
+// and beta into its bias, and corrects each output by the row's mean and
+// 1/std combined from those sums:
 //   LN(h) W^T = rstd * (h (W*gamma)^T - mean * rowsum(W*gamma)) + W beta.
-// The fp32 debug path runs LayerNorm as its own pass on fp32 buffers, and
-// GEGLU as its own pass.
+// The fp32 debug path keeps h in fp32 and runs LayerNorm as its own pass on
+// fp32 buffers, and GEGLU as its own pass.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -109,8 +110,8 @@ struct st_block {
   float2* gn_part;
   int gn_max_split;
   void* u;
-  float* h;
-  void* hcopy;  // bf16 path: [T][C] fp16 copy of h, operand of the next product
+  float* h;      // fp32 path: residual stream [T][C]
+  void* hcopy;  // bf16 path: residual stream [T][C] in fp16 (h16)
   float2* hstats;  // bf16 path: [T][C/64] sums and squared deviations of h
   void *q, *k, *vt, *o, *f;
   float* z;  // fp32 path: FF1 output before GEGLU
@@ -370,7 +371,8 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->gn_max_split = 64;
   b->gn_part = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split, "GroupNorm partials"));
   b->u = cr.alloc(T * C * es, "normalised activations");
-  b->h = static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
+  // the residual stream: fp32 on the fp32 path, fp16 (hcopy) on the bf16 path
+  b->h = b->bf16 ? nullptr : static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
   b->hcopy = b->bf16 ? cr.alloc(T * static_cast<long long>(C) * es, "fp16 residual stream") : nullptr;
   b->hstats = b->bf16 ? static_cast<float2*>(cr.alloc(T * static_cast<long long>(C / 64) * sizeof(float2),
                                                       "residual stream statistics"))
@@ -516,11 +518,22 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   auto G = [&](const GemmParams& p, int op) {
     return bf ? gemm_mfma(p, op, s) : gemm_f32(p, s);
   };
-  // bf16 path: every product that writes h also leaves it as fp16 with its
-  // per-row statistics, and the products behind a LayerNorm read that copy
-  // with the norm folded into their weights (no LayerNorm launch).
+  // bf16 path: the residual stream is kept in fp16 (h16); every product
+  // that writes it also leaves its per-row statistics, and the products
+  // behind a LayerNorm read it with the norm folded into their weights (no
+  // LayerNorm launch).
   auto keep_h = [&](GemmParams& p) {
-    if (bf) { p.epi.out_act = b->hcopy; p.epi.row_stats = b->hstats; }
+    if (!bf) return;
+    p.epi.kind = p.epi.kind == EPI_STORE_F32 ? EPI_STORE_H16 : EPI_RESID_H16;
+    p.epi.out_f32 = nullptr;
+    p.epi.out_act = b->hcopy;
+    p.epi.row_stats = b->hstats;
+  };
+  // h of the stage dump as fp32
+  auto dump_h = [&]() {
+    return bf ? f16_to_f32(b->hcopy, h_out, static_cast<long long>(T) * C, s)
+              : hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
+                               hipMemcpyDeviceToDevice, s);
   };
   auto normed = [&](GemmParams& p, const LayerDev& L, int i) {
     if (!bf) return;
@@ -544,8 +557,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   int stage = 0;
   auto dump = [&]() -> bool { return stop_stage >= 0 && stage == stop_stage; };
   if (dump()) {
-    ST_TRY(hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
-                          hipMemcpyDeviceToDevice, s), "stage copy");
+    ST_TRY(dump_h(), "stage copy");
     return ST_OK;
   }
 
@@ -659,8 +671,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
   }
   if (stop_stage >= 0) {
     if (stage != stop_stage) return fail(ST_ERR_INVALID, "stage out of range");
-    ST_TRY(hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
-                          hipMemcpyDeviceToDevice, s), "stage copy");
+    ST_TRY(dump_h(), "stage copy");
     return ST_OK;
   }
   ST_TRY(run(b, ST_K_PROJ_OUT, s, [&] {

@@ -105,21 +105,32 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
   __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
   if (C0 >= N || R0 >= M) return;
 
-  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32) {
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32 || EPI == EPI_STORE_H16 ||
+                EPI == EPI_RESID_H16) {
+    constexpr bool kH16 = EPI == EPI_STORE_H16 || EPI == EPI_RESID_H16;
+    constexpr bool kRes = EPI == EPI_RESID_F32 || EPI == EPI_RESID_H16;
     // lane -> 4 consecutive columns of one row; 4 rows per pass
     const int lc = (lane & 15) * 4;
     const float4 bias = p.epi.bias ? *reinterpret_cast<const float4*>(p.epi.bias + C0 + lc)
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    f16_t* h16 = static_cast<f16_t*>(p.epi.out_act);
     // all 16 residual rows are loaded before the first store (the compiler
     // cannot prove a store to h disjoint from the next row's load)
     float4 hin[16];
-    if constexpr (EPI == EPI_RESID_F32) {
+    if constexpr (kRes) {
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int row = R0 + it * 4 + (lane >> 4);
-        hin[it] = row < M ? *reinterpret_cast<const float4*>(
-                                p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        const long long off = static_cast<long long>(row) * p.epi.ldo + C0 + lc;
+        if constexpr (kH16) {
+          const uint2 w = row < M ? *reinterpret_cast<const uint2*>(h16 + off) : make_uint2(0u, 0u);
+          const f16x2 a = __builtin_bit_cast(f16x2, w.x), bb = __builtin_bit_cast(f16x2, w.y);
+          hin[it] = make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]),
+                                static_cast<float>(bb[0]), static_cast<float>(bb[1]));
+        } else {
+          hin[it] = row < M ? *reinterpret_cast<const float4*>(p.epi.out_f32 + off)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
 #pragma unroll
@@ -129,15 +140,25 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       if (row >= M) break;
       const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
       float4 v = make_float4(c.x + bias.x, c.y + bias.y, c.z + bias.z, c.w + bias.w);
-      if constexpr (EPI == EPI_RESID_F32) {
+      if constexpr (kRes) {
         v.x += hin[it].x; v.y += hin[it].y; v.z += hin[it].z; v.w += hin[it].w;
       }
-      *reinterpret_cast<float4*>(p.epi.out_f32 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = v;
-      if (p.epi.out_act) {
-        // the new values also as fp16 [M][ldo] (the operand of the next
-        // product)
-        f16_t* hc = static_cast<f16_t*>(p.epi.out_act) + static_cast<long long>(row) * p.epi.ldo + C0 + lc;
-        *reinterpret_cast<uint2*>(hc) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
+      const long long off = static_cast<long long>(row) * p.epi.ldo + C0 + lc;
+      if constexpr (kH16) {
+        // the stream is kept in fp16: round, store, and use the stored
+        // values below
+        const uint2 w = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
+        *reinterpret_cast<uint2*>(h16 + off) = w;
+        const f16x2 a = __builtin_bit_cast(f16x2, w.x), bb = __builtin_bit_cast(f16x2, w.y);
+        v = make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]),
+                        static_cast<float>(bb[0]), static_cast<float>(bb[1]));
+      } else {
+        *reinterpret_cast<float4*>(p.epi.out_f32 + off) = v;
+        if (h16) {
+          // the new values also as fp16 [M][ldo] (the operand of the next
+          // product)
+          *reinterpret_cast<uint2*>(h16 + off) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
+        }
       }
       if (p.epi.row_stats) {
         // the row's 64 values sit in the 16 lanes of one DPP row
@@ -632,6 +653,8 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
   switch (kind) {
     case EPI_STORE_F32: ST_PIPE_LAUNCH(EPI_STORE_F32, false) break;
     case EPI_RESID_F32: ST_PIPE_LAUNCH(EPI_RESID_F32, false) break;
+    case EPI_STORE_H16: ST_PIPE_LAUNCH(EPI_STORE_H16, false) break;
+    case EPI_RESID_H16: ST_PIPE_LAUNCH(EPI_RESID_H16, false) break;
     case EPI_NCHW: ST_PIPE_LAUNCH(EPI_NCHW, false) break;
     case EPI_HEADS:
       if (ln) { ST_PIPE_LAUNCH(EPI_HEADS, true) } else { ST_PIPE_LAUNCH(EPI_HEADS, false) }
@@ -668,7 +691,11 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
                          (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_GEGLU)))
     return hipErrorInvalidValue;
   if (p.epi.row_stats && (p.epi.ldo % 64 || p.N % 64 ||
-                          (p.epi.kind != EPI_STORE_F32 && p.epi.kind != EPI_RESID_F32)))
+                          (p.epi.kind != EPI_STORE_F32 && p.epi.kind != EPI_RESID_F32 &&
+                           p.epi.kind != EPI_STORE_H16 && p.epi.kind != EPI_RESID_H16)))
+    return hipErrorInvalidValue;
+  if ((p.epi.kind == EPI_STORE_H16 || p.epi.kind == EPI_RESID_H16) &&
+      (!p.epi.out_act || p.N % 64 || p.epi.ldo % 4))
     return hipErrorInvalidValue;
   if (p.K % 64) return hipErrorInvalidValue;
   // the DMA addresses each operand with 32-bit byte offsets

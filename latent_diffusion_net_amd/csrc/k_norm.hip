@@ -352,6 +352,19 @@ hipError_t to_f32(const void* src, bool bf16, float* dst, long long n,
   return hipGetLastError();
 }
 
+__global__ void f16_to_f32_kernel(const f16_t* __restrict__ src, float* __restrict__ dst,
+                                  long long n) {
+  long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = static_cast<float>(src[i]);
+}
+
+hipError_t f16_to_f32(const void* src, float* dst, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  f16_to_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      static_cast<const f16_t*>(src), dst, n);
+  return hipGetLastError();
+}
+
 __global__ void bf16_to_f16_kernel(uint16_t* __restrict__ buf, long long n,
                                    int* __restrict__ overflow) {
   long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;

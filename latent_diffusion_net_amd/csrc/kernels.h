@@ -13,7 +13,9 @@ enum EpiKind {
   EPI_RESID_F32 = 1,  // out_f32[row*ldo + col] += acc + bias[col]
   EPI_HEADS = 2,      // scatter into per-head Q/K (row-major) or V^T layouts
   EPI_GEGLU = 3,      // paired value/gate columns -> value * GELU(gate), fp16 out
-  EPI_NCHW = 4        // rows = channels, cols = tokens: y = acc + bias[row] + x
+  EPI_NCHW = 4,       // rows = channels, cols = tokens: y = acc + bias[row] + x
+  EPI_STORE_H16 = 5,  // out_act (fp16) [row*ldo + col] = fp16(acc + bias[col])
+  EPI_RESID_H16 = 6   // out_act (fp16) [row*ldo + col] = fp16(that value + acc + bias[col])
 };
 
 // Destination of the head-split epilogue.  Column col of the product maps to
@@ -47,9 +49,9 @@ struct EpiParams {
   int F;                  // EPI_GEGLU: value width
   int ntok;               // EPI_NCHW: tokens per sample
   HeadSplit hs;
-  // EPI_STORE_F32 / EPI_RESID_F32 (optional): per row and 64-column block of
-  // the new values, their sum and their sum of squared deviations from the
-  // block's mean, [M][ldo / 64].
+  // EPI_STORE_* / EPI_RESID_* (optional): per row and 64-column block of the
+  // new values (as stored), their sum and their sum of squared deviations
+  // from the block's mean, [M][ldo / 64].
   float2* row_stats;
   // LayerNorm folded into the product (EPI_HEADS or EPI_GEGLU, no split-K):
   // A holds h and B the weights times gamma (weight_fold_layernorm), and each
@@ -138,6 +140,8 @@ hipError_t layernorm(const float* h, const float* gamma, const float* beta,
                      void* u, int out_type, int T, int C, hipStream_t s);
 hipError_t geglu_f32(const float* z, float* f, long long T, int F,
                      hipStream_t s);
+// dst[i] = float(src[i]) (src fp16), n elements.
+hipError_t f16_to_f32(const void* src, float* dst, long long n, hipStream_t s);
 // dst[i] = float(src[i]) (src bf16 or fp32); src NULL -> dst[i] = fill.
 hipError_t to_f32(const void* src, bool bf16, float* dst, long long n,
                   float fill, hipStream_t s);
