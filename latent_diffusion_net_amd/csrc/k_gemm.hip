@@ -16,8 +16,10 @@
 // the 16 rows of one 16-lane read phase over all 16 bank groups of gfx950's
 // 64-bank LDS.  Rows beyond M or N are clamped on load and masked on store.
 //
-// The residual epilogue can also leave the new fp32 value as an fp16 copy,
-// the operand of proj_out (11 significant bits; the output is bf16).
+// The store and residual epilogues keep the residual stream either in fp32
+// (optionally with an fp16 copy) or, on the bf16 path, in fp16 only (h16,
+// 11 significant bits, the operand of the products behind the LayerNorms
+// and of proj_out), each with optional per-row sums for a folded LayerNorm.
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
