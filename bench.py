@@ -56,7 +56,9 @@ def block_flops(cfg) -> float:
 # once (bf16 storage).  proj_in's time also holds the GroupNorm apply.  On
 # the bf16 path the LayerNorms have no launch of their own (statistics in the
 # epilogues of the GEMMs that write h, normalisation folded into Q/K/V,
-# cross Q and FF1), so their row is absent and their cost sits in those rows.
+# cross Q and FF1), so their row is absent and their cost sits in those rows;
+# likewise the cross-attention when it runs in the cross Q epilogue (its
+# time is in A8, whose rate is still computed on the projection's flops).
 def row_work(cfg):
     T, C, B, N, D, F, h = cfg.T, cfg.C, cfg.B, cfg.N, cfg.D_ctx, cfg.F, cfg.heads
     return {
@@ -95,10 +97,16 @@ LAYERNORM_FOLDED = ("no launch of its own: per-row sums in the epilogues of the 
                     "write h, normalisation folded into Q/K/V, cross-attention Q and FF1")
 
 
+CROSS_ATTN_FUSED = ("no launch of its own: computed in the epilogue of the cross-attention Q "
+                    "projection (row A8, whose time includes it) when H*W is a multiple of 64")
+
+
 def row_rates(cfg, timing, copy_gbs):
     rows = {}
     if getattr(cfg, "dtype", "bf16") == "bf16" and not (timing.get("layernorm") or {}).get("launches"):
         rows["A3/A7/A12 LayerNorm"] = {"fused": LAYERNORM_FOLDED}
+    if getattr(cfg, "dtype", "bf16") == "bf16" and not (timing.get("cross_attn") or {}).get("launches"):
+        rows["A10 cross-attention"] = {"fused": CROSS_ATTN_FUSED}
     for kind, (name, bound, work) in row_work(cfg).items():
         t = timing.get(kind)
         if not t or not t["launches"]:

@@ -156,9 +156,12 @@ typedef enum {
   ST_K_QKV,          /* fused Q/K/V projection of the self-attention */
   ST_K_SELF_ATTN,    /* self-attention over the H*W tokens */
   ST_K_ATTN_OUT,     /* output projections of both attentions (+ residual) */
-  ST_K_CROSS_Q,      /* Q projection of the cross-attention */
+  ST_K_CROSS_Q,      /* Q projection of the cross-attention (bf16 storage
+                        with H*W % 64 == 0: with the cross-attention in its
+                        epilogue) */
   ST_K_CTX_KV,       /* K/V projections of the context, all layers */
-  ST_K_CROSS_ATTN,   /* cross-attention over the 77 context tokens */
+  ST_K_CROSS_ATTN,   /* cross-attention over the 77 context tokens (when
+                        it is not fused into ST_K_CROSS_Q) */
   ST_K_FF1_GEGLU,    /* first feed-forward GEMM + GEGLU */
   ST_K_FF2,          /* second feed-forward GEMM (+ residual) */
   ST_K_PROJ_OUT,     /* proj_out GEMM + tokens->NCHW + outer residual */

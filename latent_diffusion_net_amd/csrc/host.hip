@@ -11,8 +11,9 @@
 //     Q/K/V GEMM, LayerNorm 1 folded  h16, [Wq1;Wk1;Wv1]*g1 -> Q, K, V^T (per head)
 //     self-attention                Q, K, V^T             -> O [T][C] bf16
 //     out-projection GEMM           O, Wo1                -> h += .
-//     cross Q GEMM, LayerNorm 2 folded  h16, Wq2*g2       -> Q
-//     cross-attention               Q, Kc, Vc^T           -> O
+//     cross Q GEMM, LayerNorm 2 folded, with the cross-attention in its
+//       epilogue when H*W % 64 == 0   h16, Wq2*g2, Kc, Vc^T -> O
+//       (else: cross Q GEMM -> Q, then the attention kernel -> O)
 //     out-projection GEMM           O, Wo2                -> h += .
 //     FF1 GEMM+GEGLU, LayerNorm 3 folded  h16, W1*g3      -> f [T][F] fp16
 //     FF2 GEMM                      f, W2                 -> h += .
@@ -535,6 +536,9 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
               : hipMemcpyAsync(h_out, b->h, static_cast<size_t>(T) * C * sizeof(float),
                                hipMemcpyDeviceToDevice, s);
   };
+  // bf16 path with whole 64-token blocks per sample: the cross-attention
+  // runs in the epilogue of its Q projection (77 context keys)
+  const bool cross_fused = bf && N % 64 == 0;
   auto normed = [&](GemmParams& p, const LayerDev& L, int i) {
     if (!bf) return;
     p.A = b->hcopy;
@@ -613,10 +617,21 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
       ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
                return layernorm(b->h, L.ln_w[1], L.ln_b[1], b->u, act, T, C, s);
              }), "LayerNorm 2");
+    const void* kc_l = static_cast<const char*>(b->kc) + l * b->ctx_layer_stride * b->esz;
+    const void* vct_l = static_cast<const char*>(b->vct) + l * b->ctx_layer_stride * b->esz;
     ST_TRY(run(b, ST_K_CROSS_Q, s, [&] {
-             GemmParams p = gemm(b->u, C, L.wq2, C, T, C, C, EPI_HEADS);
+             GemmParams p = gemm(b->u, C, L.wq2, C, T, C, C, cross_fused ? EPI_CROSS_ATTN : EPI_HEADS);
              normed(p, L, 1);
              p.epi.bias = L.bq2;
+             if (cross_fused) {
+               // the cross-attention runs in this product's epilogue
+               p.epi.out_act = b->o; p.epi.ldo = C;
+               p.epi.ca.k = kc_l; p.epi.ca.vt = vct_l;
+               p.epi.ca.kv_pad = b->cpad; p.epi.ca.nk = ST_CTX_LEN;
+               p.epi.ca.rows_per_batch = N; p.epi.ca.heads = b->heads;
+               p.epi.ca.scale = attention_bf16_q_scale();
+               return G(p, ACT_F16);
+             }
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = nullptr; p.epi.hs.dst[2] = nullptr;
              if (bf) p.epi.hs.scale[0] = attention_bf16_q_scale();
              p.epi.hs.transposed_mask = 0; p.epi.hs.nsplit = 1; p.epi.hs.layer_stride = 0;
@@ -624,11 +639,11 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              p.epi.hs.heads = b->heads; p.epi.hs.C = C;
              return G(p, ACT_F16);
            }), "cross-attention Q projection");
-    ST_TRY(run(b, ST_K_CROSS_ATTN, s, [&] {
+    if (!cross_fused) ST_TRY(run(b, ST_K_CROSS_ATTN, s, [&] {
              AttnParams a{};
              a.q = b->q;
-             a.k = static_cast<const char*>(b->kc) + l * b->ctx_layer_stride * b->esz;
-             a.vt = static_cast<const char*>(b->vct) + l * b->ctx_layer_stride * b->esz;
+             a.k = kc_l;
+             a.vt = vct_l;
              a.o = b->o;
              a.B = B; a.heads = b->heads; a.C = C; a.Nq = N; a.Nk = ST_CTX_LEN;
              a.q_pad = b->npad; a.kv_pad = b->cpad;

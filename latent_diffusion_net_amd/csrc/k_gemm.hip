@@ -83,7 +83,135 @@ __device__ __forceinline__ float4 ln_fix(float4 a, float2 k, float4 g) {
                      fmaf(a.z, k.x, -k.y * g.z), fmaf(a.w, k.x, -k.y * g.w));
 }
 
-// Folded LayerNorm (LN: EPI_HEADS and EPI_GEGLU only):
+// Key order of a 32-key block of the fused cross-attention: row r of the K
+// operand holds key kperm(r) (bits 2 and 3 of r swapped), so that the eight
+// scores the accumulator layout gives one lane for one P.V step are eight
+// consecutive keys, the keys of one 16-byte V^T operand.
+__device__ __forceinline__ int kperm(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// EPI_CROSS_ATTN for one 64x64 block (64 queries of one sample, one head):
+// Q = (acc [LayerNorm-corrected] + bias) * scale is staged in LDS and read
+// back as bf16 B operands; for each 32-query half, S^T = K Q^T over three
+// 32-key blocks (keys >= nk masked), an exact one-pass softmax in base 2,
+// O^T = V^T P^T over six 16-key steps, O normalised and stored as bf16.  The
+// K and V^T operands come straight from memory (L2: 24 KB per sample and
+// head), requested before the staging.
+template <bool LN>
+__device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floatx16 (&acc)[2][2],
+                                                 int R0, int C0, int lane, float* stage,
+                                                 const float2* ln_rows, const float* ln_cols) {
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const CrossAttn& ca = p.epi.ca;
+  if (R0 >= p.M || C0 >= p.N) return;
+  const long long bh = static_cast<long long>(R0 / ca.rows_per_batch) * ca.heads + (C0 >> 6);
+  const uint16_t* Kh = static_cast<const uint16_t*>(ca.k) + bh * ca.kv_pad * kHeadDim;
+  const uint16_t* Vh = static_cast<const uint16_t*>(ca.vt) + bh * kHeadDim * ca.kv_pad;
+  uint4 kop[3][4], vop[2][6];
+#pragma unroll
+  for (int kb = 0; kb < 3; ++kb)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      kop[kb][s4] = *reinterpret_cast<const uint4*>(Kh + (kb * 32 + kperm(l32)) * kHeadDim + 16 * s4 + 8 * lhi);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int st = 0; st < 6; ++st)
+      vop[db][st] = *reinterpret_cast<const uint4*>(
+          Vh + static_cast<long long>(db * 32 + l32) * ca.kv_pad + 16 * st + 8 * lhi);
+  float bj[2], gj[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bj[j] = p.epi.bias ? p.epi.bias[C0 + j * 32 + l32] : 0.f;
+    if constexpr (LN) gj[j] = ln_cols[j * 32 + l32];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
+      float2 k = make_float2(1.f, 0.f);
+      if constexpr (LN) k = ln_rows[lr];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v = acc[i][j][r];
+        if constexpr (LN) v = fmaf(v, k.x, -k.y * gj[j]);
+        stage[stg(lr, j * 32 + l32)] = (v + bj[j]) * ca.scale;
+      }
+    }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
+  bf16x2 one;
+  one[0] = static_cast<__bf16>(1.0f);
+  one[1] = static_cast<__bf16>(1.0f);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int lr = qb * 32 + l32;  // this lane's query within the block
+    uint4 qop[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float4 a = *reinterpret_cast<const float4*>(&stage[stg(lr, 16 * s4 + 8 * lhi)]);
+      const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, 16 * s4 + 8 * lhi + 4)]);
+      qop[s4] = make_uint4(pack2bf(a.x, a.y), pack2bf(a.z, a.w), pack2bf(c.x, c.y), pack2bf(c.z, c.w));
+    }
+    floatx16 sc[3];
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) sc[kb] = mfma32x32x16(kop[kb][s4], qop[s4], sc[kb], bf16_t{});
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (kb * 32 + kperm(8 * (r >> 2) + 4 * lhi + (r & 3)) >= ca.nk) sc[kb][r] = -INFINITY;
+        mx = fmaxf(mx, sc[kb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // P^T step st: block st / 2, entries 8 (st % 2) + 0..7 = keys 16 st + 8 lhi + 0..7
+    uint4 pb[6];
+    float ps = 0.f;
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x2 pk;
+        pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj] - mx));
+        pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj + 1] - mx));
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ps, false);
+        w[jj] = __builtin_bit_cast(uint32_t, pk);
+      }
+      pb[st] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    const float inv = 1.0f / (ps + __shfl_xor(ps, 32, 64));
+    floatx16 o[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 6; ++st) o[db] = mfma32x32x16(vop[db][st], pb[st], o[db], bf16_t{});
+    }
+    // O^T: this lane holds query lr, dims db*32 + 8g + 4lhi + 0..3
+    const int row = R0 + lr;
+    if (row < p.M) {
+      uint16_t* orow = static_cast<uint16_t*>(p.epi.out_act) + static_cast<long long>(row) * p.epi.ldo + C0;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * lhi) =
+              make_uint2(pack2bf(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                         pack2bf(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+    }
+  }
+}
+
+// Folded LayerNorm (LN: EPI_HEADS, EPI_GEGLU and EPI_CROSS_ATTN only):
 // ln_rows (LDS) holds (rstd, mean * rstd) for the 64 rows of this block and
 // ln_cols (LDS) the folded weights' sums for its 64 columns; each value read
 // back from the staging tile becomes rstd * acc - mean * rstd * g.
@@ -93,7 +221,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
                                              int m0, int n0, int wm, int wn,
                                              int lane, float* stage,
                                              const float2* ln_rows, const float* ln_cols) {
-  static_assert(!LN || EPI == EPI_HEADS || EPI == EPI_GEGLU, "folded LayerNorm kinds");
+  static_assert(!LN || EPI == EPI_HEADS || EPI == EPI_GEGLU || EPI == EPI_CROSS_ATTN,
+                "folded LayerNorm kinds");
+  if constexpr (EPI == EPI_CROSS_ATTN) {
+    cross_attn_block<LN>(p, acc, m0 + wm * 64, n0 + wn * 64, lane, stage, ln_rows, ln_cols);
+    return;
+  }
   const int l32 = lane & 31, lhi = lane >> 5;
   const int M = p.M, N = p.N;
   const int R0 = m0 + wm * 64, C0 = n0 + wn * 64;
@@ -664,6 +797,13 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
     case EPI_GEGLU:
       if (ln) { ST_PIPE_LAUNCH(EPI_GEGLU, true) } else { ST_PIPE_LAUNCH(EPI_GEGLU, false) }
       break;
+    case EPI_CROSS_ATTN:  // 64x64 wavefront tiles only (gemm_mfma picks them)
+      if constexpr (FM == 2 && FN == 2) {
+        if (ln) { ST_PIPE_LAUNCH(EPI_CROSS_ATTN, true) } else { ST_PIPE_LAUNCH(EPI_CROSS_ATTN, false) }
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -690,7 +830,13 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.n_off != 0) return hipErrorInvalidValue;
   if (p.epi.ln_stats && (!p.epi.ln_g || p.epi.ln_blocks * 64 != p.K ||
-                         (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_GEGLU)))
+                         (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_GEGLU &&
+                          p.epi.kind != EPI_CROSS_ATTN)))
+    return hipErrorInvalidValue;
+  if (p.epi.kind == EPI_CROSS_ATTN &&
+      (!p.epi.ca.k || !p.epi.ca.vt || !p.epi.out_act || p.epi.ca.nk < 1 || p.epi.ca.nk > 96 ||
+       p.epi.ca.kv_pad < 96 || p.epi.ca.rows_per_batch <= 0 || p.epi.ca.rows_per_batch % 64 ||
+       p.N % 64 || p.epi.ldo % 4 || p.N != p.epi.ca.heads * 64))
     return hipErrorInvalidValue;
   if (p.epi.row_stats && (p.epi.ldo % 64 || p.N % 64 ||
                           (p.epi.kind != EPI_STORE_F32 && p.epi.kind != EPI_RESID_F32 &&
@@ -722,7 +868,8 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   // them to give most CUs one; otherwise 128x128 tiles, two per CU.
   const int mtb = (p.M + 255) / 256, ntb = (p.N + 255) / 256;
   const long long big_tiles = static_cast<long long>(mtb) * ntb;
-  if (big_tiles < kBigTileMin) return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
+  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN)
+    return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
   // When the last round of large tiles would leave more than a quarter of
   // the CUs idle, the columns of whole rounds take large tiles and the rest
   // 128x128 tiles (two per CU) in a second launch.

@@ -15,7 +15,24 @@ enum EpiKind {
   EPI_GEGLU = 3,      // paired value/gate columns -> value * GELU(gate), fp16 out
   EPI_NCHW = 4,       // rows = channels, cols = tokens: y = acc + bias[row] + x
   EPI_STORE_H16 = 5,  // out_act (fp16) [row*ldo + col] = fp16(acc + bias[col])
-  EPI_RESID_H16 = 6   // out_act (fp16) [row*ldo + col] = fp16(that value + acc + bias[col])
+  EPI_RESID_H16 = 6,  // out_act (fp16) [row*ldo + col] = fp16(that value + acc + bias[col])
+  EPI_CROSS_ATTN = 7  // the product is Q of the cross-attention: attend (CrossAttn)
+};
+
+// Cross-attention in the epilogue of its Q projection (EPI_CROSS_ATTN).
+// Column col of the product is dimension col % 64 of head col / 64; row r is
+// query n = r % rows_per_batch of sample r / rows_per_batch, and every
+// 64-row block of the product must lie in one sample (rows_per_batch % 64 ==
+// 0).  Q = (acc + bias) * scale is rounded to bf16 and attends over the nk
+// <= 96 keys of k [B*heads][kv_pad][64] and vt [B*heads][64][kv_pad] (bf16,
+// kv_pad >= 96, padding finite) with softmax base 2 (scale includes
+// log2(e)); O goes to o [M][ldo] bf16, columns as in the product.
+struct CrossAttn {
+  const void* k;
+  const void* vt;
+  int kv_pad, nk;
+  int rows_per_batch, heads;
+  float scale;
 };
 
 // Destination of the head-split epilogue.  Column col of the product maps to
@@ -62,6 +79,7 @@ struct EpiParams {
   const float* ln_g;
   int ln_blocks;
   float ln_eps;
+  CrossAttn ca;  // EPI_CROSS_ATTN (output: out_act, row stride ldo)
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T, then the epilogue.

@@ -119,3 +119,4 @@ def test_row_rates_units(bench):
     # bf16 path without LayerNorm launches: the row says where the work went
     r2 = bench.row_rates(cfg, {"self_attn": {"ms": 0.2, "launches": 2}}, 5000.0)
     assert r2["A3/A7/A12 LayerNorm"] == {"fused": bench.LAYERNORM_FOLDED}
+    assert r2["A10 cross-attention"] == {"fused": bench.CROSS_ATTN_FUSED}
