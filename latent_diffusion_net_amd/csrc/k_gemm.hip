@@ -162,20 +162,27 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) sc[kb] = mfma32x32x16(kop[kb][s4], qop[s4], sc[kb], bf16_t{});
     }
+    // keys >= nk (nk > 64: only the third block has any) -> -inf
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (kb * 32 + kperm(8 * (r >> 2) + 4 * lhi + (r & 3)) >= ca.nk) sc[kb][r] = -INFINITY;
+        if (kb == 2 && 64 + kperm(8 * (r >> 2) + 4 * lhi + (r & 3)) >= ca.nk) sc[kb][r] = -INFINITY;
         mx = fmaxf(mx, sc[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // P^T step st: block st / 2, entries 8 (st % 2) + 0..7 = keys 16 st + 8 lhi + 0..7
+    // P^T step st: block st / 2, entries 8 (st % 2) + 0..7 = keys 16 st + 8 lhi + 0..7;
+    // steps past the last key are zero and skipped
+    const int nsteps = (ca.nk + 15) >> 4;
     uint4 pb[6];
     float ps = 0.f;
 #pragma unroll
     for (int st = 0; st < 6; ++st) {
+      if (st >= nsteps) {
+        pb[st] = make_uint4(0u, 0u, 0u, 0u);
+        continue;
+      }
       uint32_t w[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -194,7 +201,8 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 #pragma unroll
-      for (int st = 0; st < 6; ++st) o[db] = mfma32x32x16(vop[db][st], pb[st], o[db], bf16_t{});
+      for (int st = 0; st < 6; ++st)
+        if (st < nsteps) o[db] = mfma32x32x16(vop[db][st], pb[st], o[db], bf16_t{});
     }
     // O^T: this lane holds query lr, dims db*32 + 8g + 4lhi + 0..3
     const int row = R0 + lr;
@@ -834,7 +842,7 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
                           p.epi.kind != EPI_CROSS_ATTN)))
     return hipErrorInvalidValue;
   if (p.epi.kind == EPI_CROSS_ATTN &&
-      (!p.epi.ca.k || !p.epi.ca.vt || !p.epi.out_act || p.epi.ca.nk < 1 || p.epi.ca.nk > 96 ||
+      (!p.epi.ca.k || !p.epi.ca.vt || !p.epi.out_act || p.epi.ca.nk <= 64 || p.epi.ca.nk > 96 ||
        p.epi.ca.kv_pad < 96 || p.epi.ca.rows_per_batch <= 0 || p.epi.ca.rows_per_batch % 64 ||
        p.N % 64 || p.epi.ldo % 4 || p.N != p.epi.ca.heads * 64))
     return hipErrorInvalidValue;

@@ -24,7 +24,7 @@ enum EpiKind {
 // query n = r % rows_per_batch of sample r / rows_per_batch, and every
 // 64-row block of the product must lie in one sample (rows_per_batch % 64 ==
 // 0).  Q = (acc + bias) * scale is rounded to bf16 and attends over the nk
-// <= 96 keys of k [B*heads][kv_pad][64] and vt [B*heads][64][kv_pad] (bf16,
+// keys (64 < nk <= 96) of k [B*heads][kv_pad][64] and vt [B*heads][64][kv_pad] (bf16,
 // kv_pad >= 96, padding finite) with softmax base 2 (scale includes
 // log2(e)); O goes to o [M][ldo] bf16, columns as in the product.
 struct CrossAttn {
