@@ -107,10 +107,16 @@ def test_small_stress(spec, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_sharp_softmax(dtype):
+@pytest.mark.parametrize("grid", [(1, 20, 20), (2, 8, 8), (1, 24, 24)],
+                         ids=["b1_20x20", "b2_8x8", "b1_24x24"])
+def test_sharp_softmax(dtype, grid):
     """Large weights: logits spread over tens of units, so the online softmax
-    rescales often and the row maxima matter."""
-    cfg = synth.BlockConfig("sharp_" + dtype, 1, 128, 20, 20, 2, 128, 1, dtype)
+    rescales often and the row maxima matter.  400 tokens run the
+    cross-attention as its own kernel; 2 x 64 tokens (a multiple of 64 per
+    sample) run it inside the Q projection's epilogue, with GEMM tiles that
+    span both samples; 576 tokens too, ending half-way into a 128-row tile."""
+    B, H, W = grid
+    cfg = synth.BlockConfig(f"sharp_{B}x{H}x{W}_" + dtype, B, 128, H, W, 2, 128, 1, dtype)
     inp = synth.make_inputs(cfg, 5, weight_std=0.12)
     yo, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
                                  intermediates=True)
@@ -119,7 +125,7 @@ def test_sharp_softmax(dtype):
     for s, key in ((1, "l0_sa"), (2, "l0_ca")):
         # the sublayer's own contribution, relative
         prev = inter["h0"] if s == 1 else inter["l0_sa"]
-        r = rel_l2(hs[s] - prev, inter[key] - prev)
+        r = rel_l2(hs[s].reshape(prev.shape) - prev, inter[key] - prev)
         _say(f"    stage {s}: update rel_l2={r:.3e}")
         assert r <= (tol if dtype == "bf16" else 1e-4), r
     assert rel_l2(y, yo) <= (1e-2 if dtype == "bf16" else 1e-5)
