@@ -73,7 +73,7 @@ __device__ __forceinline__ int perm(int r) {
 // QB: 32-row query blocks per wavefront; NW: wavefronts per workgroup.
 // KIND only gives self- and cross-attention their own kernel symbols.
 template <int KIND, int QB, int NW>
-__global__ __launch_bounds__(64 * NW, QB == 1 ? 3 : 2) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16_kernel(AttnParams p) {
   constexpr int QW = 32 * QB;   // query rows per wavefront
   constexpr int QT = QW * NW;   // query rows per workgroup
   constexpr int BPW = 8 / NW;   // 1 KB DMA blocks of each 8 KB tile per wavefront
@@ -578,6 +578,20 @@ void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full,
   nsplit = sp;
 }
 
+// Compute units of the current device (cached per device).
+static int attn_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
   const int qtiles = (p.Nq + kQT - 1) / kQT;
   const int tiles = p.B * p.heads * qtiles;
@@ -588,6 +602,17 @@ hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
     if (!p.part || p.n_full < 0 || p.n_full >= tiles || (p.Nk + KT - 1) / KT < p.nsplit)
       return hipErrorInvalidValue;
     grid = p.n_full + (tiles - p.n_full) * p.nsplit;
+  }
+  // Few query tiles (short sequences, no key split): workgroups of two
+  // wavefronts (64 queries) instead, twice as many, so that more CUs and
+  // more wavefronts per SIMD take part.
+  if (p.nsplit <= 1 && tiles < 2 * attn_cu_count()) {
+    const int grid64 = p.B * p.heads * ((p.Nq + 63) / 64);
+    if (p.Nk == kCtxLen)
+      attn_bf16_kernel<1, 1, 2><<<grid64, 128, 0, s>>>(p);
+    else
+      attn_bf16_kernel<0, 1, 2><<<grid64, 128, 0, s>>>(p);
+    return hipGetLastError();
   }
   if (p.Nk == kCtxLen)
     attn_bf16_kernel<1, kQB, kNW><<<grid, 64 * kNW, 0, s>>>(p);
