@@ -219,16 +219,19 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
   }
 }
 
+// PF (EPI_RESID_H16): the residual values of this lane's 16 rows arrive in
+// resv (read from LDS after the main loop) instead of from memory.
 // Folded LayerNorm (LN: EPI_HEADS, EPI_GEGLU and EPI_CROSS_ATTN only):
 // ln_rows (LDS) holds (rstd, mean * rstd) for the 64 rows of this block and
 // ln_cols (LDS) the folded weights' sums for its 64 columns; each value read
 // back from the staging tile becomes rstd * acc - mean * rstd * g.
-template <int EPI, bool LN>
+template <int EPI, bool LN, bool PF = false>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
                                              const floatx16 (&acc)[2][2],
                                              int m0, int n0, int wm, int wn,
                                              int lane, float* stage,
-                                             const float2* ln_rows, const float* ln_cols) {
+                                             const float2* ln_rows, const float* ln_cols,
+                                             const uint2 (&resv)[16]) {
   static_assert(!LN || EPI == EPI_HEADS || EPI == EPI_GEGLU || EPI == EPI_CROSS_ATTN,
                 "folded LayerNorm kinds");
   if constexpr (EPI == EPI_CROSS_ATTN) {
@@ -266,7 +269,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         const int row = R0 + it * 4 + (lane >> 4);
         const long long off = static_cast<long long>(row) * p.epi.ldo + C0 + lc;
         if constexpr (kH16) {
-          const uint2 w = row < M ? *reinterpret_cast<const uint2*>(h16 + off) : make_uint2(0u, 0u);
+          uint2 w;
+          if constexpr (PF) w = resv[it];  // prefetched during the last stage
+          else w = row < M ? *reinterpret_cast<const uint2*>(h16 + off) : make_uint2(0u, 0u);
           const f16x2 a = __builtin_bit_cast(f16x2, w.x), bb = __builtin_bit_cast(f16x2, w.y);
           hin[it] = make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]),
                                 static_cast<float>(bb[0]), static_cast<float>(bb[1]));
@@ -673,10 +678,30 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     const float rstd = rsqrtf(var + p.epi.ln_eps);
     if (!half) ln_tab[t >> 1] = make_float2(rstd, static_cast<float>(mean) * rstd);
   }
+  // Residual prefetch (EPI_RESID_H16, 128x128 tiles): at the top of the
+  // last stage, the stage buffers that stage does not read (32 KB: one
+  // 128x128 fp16 tile, rows 0-63 in the A buffer and 64-127 in the B
+  // buffer) receive the tile's residual values by LDS DMA (rows past M read
+  // as zero), which land while the last stage computes; each wavefront then
+  // takes its 64x64 part into registers before the buffers hold the
+  // epilogue tiles.
+  constexpr bool kPF = EPI == EPI_RESID_H16 && WM == 2 && WN == 2 && FM == 2 && FN == 2;
+  auto issue_res = [&](uint16_t* wa, uint16_t* wb) {
+    const long long lim = static_cast<long long>(M) * p.epi.ldo * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = wave * 8 + j;  // rows 4 blk .. 4 blk + 3, 16 lanes per row
+      const long long off = (static_cast<long long>(m0 + 4 * blk + (lane >> 4)) * p.epi.ldo + n0 +
+                             (lane & 15) * 8) * 2;
+      dma16(p.epi.out_act, static_cast<int>(lim), blk < 16 ? wa + blk * 512 : wb + (blk - 16) * 512,
+            static_cast<unsigned>(off < lim ? off : lim), 0);
+    }
+  };
   auto stage = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
     wait_vmcnt_lds<0>();
     stage_barrier();
     if (k + 1 < nk) issue(k + 1, wa, wb);
+    else if (kPF) issue_res(wa, wb);
     steps(ca, cb);
   };
   for (int k = 0; k < nk; k += 2) {
@@ -684,9 +709,21 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
   }
 
+  uint2 resv[16];
+  uint16_t* ra = ((nk - 1) & 1) ? sA0 : sA1;
+  uint16_t* rb = ((nk - 1) & 1) ? sB0 : sB1;
+  if constexpr (kPF) wait_vmcnt_lds<0>();  // the residual tile has landed
+
   // every wavefront is done reading the stage buffers before they hold
   // the epilogue tiles
   stage_barrier();
+  if constexpr (kPF) {
+    const uint16_t* rt = (wm ? rb : ra) + wn * 64 + (lane & 15) * 4;
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+      resv[it] = *reinterpret_cast<const uint2*>(rt + (it * 4 + (lane >> 4)) * 128);
+    stage_barrier();
+  }
   // 16 KB per wavefront: the stage buffers taken in order
   float* stg_area;
   {
@@ -716,10 +753,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
                                   {acc[2 * si + 1][2 * sj], acc[2 * si + 1][2 * sj + 1]}};
       const int r0 = m0 + wm * FM * 32 + si * 64, c0 = n0 + wn * FN * 32 + sj * 64;
       if (p.ksplit > 1)
-        epilogue_lds<EPI_STORE_F32, false>(q, sub, r0, c0, 0, 0, lane, stg_area, nullptr, nullptr);
+        epilogue_lds<EPI_STORE_F32, false>(q, sub, r0, c0, 0, 0, lane, stg_area, nullptr, nullptr, resv);
       else
-        epilogue_lds<EPI, LN>(p, sub, r0, c0, 0, 0, lane, stg_area, ln_tab + (r0 - m0),
-                              ln_gtab + (c0 - n0));
+        epilogue_lds<EPI, LN, kPF>(p, sub, r0, c0, 0, 0, lane, stg_area, ln_tab + (r0 - m0),
+                                   ln_gtab + (c0 - n0), resv);
     }
 }
 
