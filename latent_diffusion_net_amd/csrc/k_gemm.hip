@@ -387,20 +387,21 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         *reinterpret_cast<uint2*>(base + (bh * hs.npad + n) * kHeadDim + lc) = pk;
       }
     } else {
-      // V^T [bh][64][npad]: lane -> one dim, 4 consecutive tokens
+      // V^T [bh][64][npad]: lane -> one dim, 8 consecutive tokens (one
+      // 16-byte store)
       const int dim = lane;
       const float bb = bias ? bias[dim] : 0.f;
       float lg = 0.f;
       if constexpr (LN) lg = ln_cols[dim];
-      const bool vec = (hs.rows_per_batch & 3) == 0;
-#pragma unroll 2
-      for (int it = 0; it < 16; ++it) {
-        const int lr0 = it * 4;
+      const bool vec = (hs.rows_per_batch & 7) == 0;
+#pragma unroll 1
+      for (int it = 0; it < 8; ++it) {
+        const int lr0 = it * 8;
         const int row0 = R0 + lr0;
         if (row0 >= M) break;
-        float v[4];
+        float v[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
           float a = stage[stg(lr0 + k, dim)];
           if constexpr (LN) {
             const float2 kk = ln_rows[lr0 + k];
@@ -408,15 +409,16 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
           }
           v[k] = (a + bb) * sc;
         }
-        if (vec && row0 + 3 < M) {
+        if (vec && row0 + 7 < M) {
           const int b = row0 / hs.rows_per_batch;
           const int n = row0 - b * hs.rows_per_batch;
           const long long bh = static_cast<long long>(b) * hs.heads + head;
-          *reinterpret_cast<uint2*>(base + (bh * kHeadDim + dim) * hs.npad + n) =
-              make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
+          *reinterpret_cast<uint4*>(base + (bh * kHeadDim + dim) * hs.npad + n) =
+              make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]),
+                         pack2bf(v[6], v[7]));
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < 8; ++k) {
             const int row = row0 + k;
             if (row >= M) break;
             const int b = row / hs.rows_per_batch;
