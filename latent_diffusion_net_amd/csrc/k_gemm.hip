@@ -365,26 +365,37 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
     const float* bias = p.epi.bias ? p.epi.bias + C0 : nullptr;
     const float sc = hs.scale[sp];
     if (!((hs.transposed_mask >> sp) & 1)) {
-      // [bh][n][64]: lane -> 4 consecutive dims of one token
-      const int lc = (lane & 15) * 4;
-      float bb[4];
+      // [bh][n][64]: lane -> 8 consecutive dims of one token (one 16-byte
+      // store), 8 tokens per pass
+      const int lc = (lane & 7) * 8;
+      float bb[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bb[k] = bias ? bias[lc + k] : 0.f;
-      float4 lg = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (LN) lg = *reinterpret_cast<const float4*>(ln_cols + lc);
-#pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int lr = it * 4 + (lane >> 4);
+      for (int k = 0; k < 8; ++k) bb[k] = bias ? bias[lc + k] : 0.f;
+      float4 lg[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+      if constexpr (LN) {
+        lg[0] = *reinterpret_cast<const float4*>(ln_cols + lc);
+        lg[1] = *reinterpret_cast<const float4*>(ln_cols + lc + 4);
+      }
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int lr = it * 8 + (lane >> 3);
         const int row = R0 + lr;
         if (row >= M) break;
         const int b = row / hs.rows_per_batch;
         const int n = row - b * hs.rows_per_batch;
-        float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
-        if constexpr (LN) c = ln_fix(c, ln_rows[lr], lg);
-        const uint2 pk = make_uint2(pack2bf((c.x + bb[0]) * sc, (c.y + bb[1]) * sc),
-                                    pack2bf((c.z + bb[2]) * sc, (c.w + bb[3]) * sc));
+        float4 c0 = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+        float4 c1 = *reinterpret_cast<const float4*>(&stage[stg(lr, lc + 4)]);
+        if constexpr (LN) {
+          const float2 k = ln_rows[lr];
+          c0 = ln_fix(c0, k, lg[0]);
+          c1 = ln_fix(c1, k, lg[1]);
+        }
+        const uint4 pk = make_uint4(pack2bf((c0.x + bb[0]) * sc, (c0.y + bb[1]) * sc),
+                                    pack2bf((c0.z + bb[2]) * sc, (c0.w + bb[3]) * sc),
+                                    pack2bf((c1.x + bb[4]) * sc, (c1.y + bb[5]) * sc),
+                                    pack2bf((c1.z + bb[6]) * sc, (c1.w + bb[7]) * sc));
         const long long bh = static_cast<long long>(b) * hs.heads + head;
-        *reinterpret_cast<uint2*>(base + (bh * hs.npad + n) * kHeadDim + lc) = pk;
+        *reinterpret_cast<uint4*>(base + (bh * hs.npad + n) * kHeadDim + lc) = pk;
       }
     } else {
       // V^T [bh][64][npad]: lane -> one dim, 8 consecutive tokens (one
