@@ -68,6 +68,14 @@ __device__ __forceinline__ int stg(int row, int col) {
   return row * 64 + (col ^ (((row >> 2) & 1) << 5));
 }
 
+// Sum over the 8 lanes of half a DPP row; each of them gets the sum.
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  return v;
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
@@ -219,8 +227,8 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
   }
 }
 
-// PF (EPI_RESID_H16): the residual values of this lane's 16 rows arrive in
-// resv (read from LDS after the main loop) instead of from memory.
+// PF (EPI_RESID_H16): the residual values of this lane's 8 rows x 8 columns
+// arrive in resv (read from LDS after the main loop) instead of from memory.
 // Folded LayerNorm (LN: EPI_HEADS, EPI_GEGLU and EPI_CROSS_ATTN only):
 // ln_rows (LDS) holds (rstd, mean * rstd) for the 64 rows of this block and
 // ln_cols (LDS) the folded weights' sums for its 64 columns; each value read
@@ -231,7 +239,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
                                              int m0, int n0, int wm, int wn,
                                              int lane, float* stage,
                                              const float2* ln_rows, const float* ln_cols,
-                                             const uint2 (&resv)[16]) {
+                                             const uint4 (&resv)[8]) {
   static_assert(!LN || EPI == EPI_HEADS || EPI == EPI_GEGLU || EPI == EPI_CROSS_ATTN,
                 "folded LayerNorm kinds");
   if constexpr (EPI == EPI_CROSS_ATTN) {
@@ -251,10 +259,80 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
   __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
   if (C0 >= N || R0 >= M) return;
 
-  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32 || EPI == EPI_STORE_H16 ||
-                EPI == EPI_RESID_H16) {
-    constexpr bool kH16 = EPI == EPI_STORE_H16 || EPI == EPI_RESID_H16;
-    constexpr bool kRes = EPI == EPI_RESID_F32 || EPI == EPI_RESID_H16;
+  if constexpr (EPI == EPI_STORE_H16 || EPI == EPI_RESID_H16) {
+    // The stream is kept in fp16: lane -> 8 consecutive columns of one row
+    // (one 16-byte store), 8 rows per pass; the row sums use the stored
+    // (rounded) values.
+    constexpr bool kRes = EPI == EPI_RESID_H16;
+    const int lc = (lane & 7) * 8;
+    float bias[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bias[k] = 0.f;
+    if (p.epi.bias) {
+      const float4 b0 = *reinterpret_cast<const float4*>(p.epi.bias + C0 + lc);
+      const float4 b1 = *reinterpret_cast<const float4*>(p.epi.bias + C0 + lc + 4);
+      bias[0] = b0.x; bias[1] = b0.y; bias[2] = b0.z; bias[3] = b0.w;
+      bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
+    }
+    f16_t* h16 = static_cast<f16_t*>(p.epi.out_act);
+    // all residual rows are loaded before the first store (the compiler
+    // cannot prove a store to h disjoint from the next row's load)
+    uint4 hin[8];
+    if constexpr (kRes) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = R0 + it * 8 + (lane >> 3);
+        if constexpr (PF) {
+          hin[it] = resv[it];  // prefetched during the last stage
+        } else {
+          hin[it] = row < M ? *reinterpret_cast<const uint4*>(h16 + static_cast<long long>(row) * p.epi.ldo + C0 + lc)
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int lr = it * 8 + (lane >> 3);
+      const int row = R0 + lr;
+      if (row >= M) break;
+      const float4 c0 = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&stage[stg(lr, lc + 4)]);
+      float v[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += bias[k];
+      if constexpr (kRes) {
+        const uint32_t hw[4] = {hin[it].x, hin[it].y, hin[it].z, hin[it].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f16x2 h2 = __builtin_bit_cast(f16x2, hw[k]);
+          v[2 * k] += static_cast<float>(h2[0]);
+          v[2 * k + 1] += static_cast<float>(h2[1]);
+        }
+      }
+      const uint4 w = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]), pack2h(v[4], v[5]),
+                                 pack2h(v[6], v[7]));
+      *reinterpret_cast<uint4*>(h16 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = w;
+      if (p.epi.row_stats) {
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f16x2 h2 = __builtin_bit_cast(f16x2, ww[k]);
+          v[2 * k] = static_cast<float>(h2[0]);
+          v[2 * k + 1] = static_cast<float>(h2[1]);
+        }
+        // the row's 64 values sit in 8 lanes (half a DPP row)
+        const float sum = row8_sum(((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+        const float mb = sum * (1.0f / 64.0f);
+        float q = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q = fmaf(v[k] - mb, v[k] - mb, q);
+        const float m2 = row8_sum(q);
+        if ((lane & 7) == 0)
+          p.epi.row_stats[static_cast<long long>(row) * (p.epi.ldo >> 6) + (C0 >> 6)] = make_float2(sum, m2);
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32) {
+    constexpr bool kRes = EPI == EPI_RESID_F32;
     // lane -> 4 consecutive columns of one row; 4 rows per pass
     const int lc = (lane & 15) * 4;
     const float4 bias = p.epi.bias ? *reinterpret_cast<const float4*>(p.epi.bias + C0 + lc)
@@ -268,17 +346,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       for (int it = 0; it < 16; ++it) {
         const int row = R0 + it * 4 + (lane >> 4);
         const long long off = static_cast<long long>(row) * p.epi.ldo + C0 + lc;
-        if constexpr (kH16) {
-          uint2 w;
-          if constexpr (PF) w = resv[it];  // prefetched during the last stage
-          else w = row < M ? *reinterpret_cast<const uint2*>(h16 + off) : make_uint2(0u, 0u);
-          const f16x2 a = __builtin_bit_cast(f16x2, w.x), bb = __builtin_bit_cast(f16x2, w.y);
-          hin[it] = make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]),
-                                static_cast<float>(bb[0]), static_cast<float>(bb[1]));
-        } else {
-          hin[it] = row < M ? *reinterpret_cast<const float4*>(p.epi.out_f32 + off)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        hin[it] = row < M ? *reinterpret_cast<const float4*>(p.epi.out_f32 + off)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
 #pragma unroll
@@ -292,21 +361,11 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         v.x += hin[it].x; v.y += hin[it].y; v.z += hin[it].z; v.w += hin[it].w;
       }
       const long long off = static_cast<long long>(row) * p.epi.ldo + C0 + lc;
-      if constexpr (kH16) {
-        // the stream is kept in fp16: round, store, and use the stored
-        // values below
-        const uint2 w = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
-        *reinterpret_cast<uint2*>(h16 + off) = w;
-        const f16x2 a = __builtin_bit_cast(f16x2, w.x), bb = __builtin_bit_cast(f16x2, w.y);
-        v = make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]),
-                        static_cast<float>(bb[0]), static_cast<float>(bb[1]));
-      } else {
-        *reinterpret_cast<float4*>(p.epi.out_f32 + off) = v;
-        if (h16) {
-          // the new values also as fp16 [M][ldo] (the operand of the next
-          // product)
-          *reinterpret_cast<uint2*>(h16 + off) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
-        }
+      *reinterpret_cast<float4*>(p.epi.out_f32 + off) = v;
+      if (h16) {
+        // the new values also as fp16 [M][ldo] (the operand of the next
+        // product)
+        *reinterpret_cast<uint2*>(h16 + off) = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
       }
       if (p.epi.row_stats) {
         // the row's 64 values sit in the 16 lanes of one DPP row
@@ -722,7 +781,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
   }
 
-  uint2 resv[16];
+  uint4 resv[8];
   uint16_t* ra = ((nk - 1) & 1) ? sA0 : sA1;
   uint16_t* rb = ((nk - 1) & 1) ? sB0 : sB1;
   if constexpr (kPF) wait_vmcnt_lds<0>();  // the residual tile has landed
@@ -731,10 +790,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   // the epilogue tiles
   stage_barrier();
   if constexpr (kPF) {
-    const uint16_t* rt = (wm ? rb : ra) + wn * 64 + (lane & 15) * 4;
+    const uint16_t* rt = (wm ? rb : ra) + wn * 64 + (lane & 7) * 8;
 #pragma unroll
-    for (int it = 0; it < 16; ++it)
-      resv[it] = *reinterpret_cast<const uint2*>(rt + (it * 4 + (lane >> 4)) * 128);
+    for (int it = 0; it < 8; ++it)
+      resv[it] = *reinterpret_cast<const uint4*>(rt + (it * 8 + (lane >> 3)) * 128);
     stage_barrier();
   }
   // 16 KB per wavefront: the stage buffers taken in order
