@@ -17,6 +17,7 @@
 //     out-projection GEMM           O, Wo2                -> h += .
 //     FF1 GEMM+GEGLU, LayerNorm 3 folded  h16, W1*g3      -> f [T][F] fp16
 //     FF2 GEMM                      f, W2                 -> h += .
+//       (with few [T][C] output tiles: K slices, then their ordered sum)
 //   proj_out GEMM, transposed       W_out, h16            -> y = NCHW(.) + x
 // The residual stream h lives in fp16 (h16).  Every GEMM that writes it
 // (proj_in and the three residual products) also writes, per row and 64
@@ -122,6 +123,11 @@ struct st_block {
   float* attn_part;
   int ctx_ksplit;   // bf16 path: K slices of the context K/V GEMM (1 = none)
   float* ctx_ws;    // [ctx_ksplit][B*77][depth*2C] fp32 partial products
+  // bf16 path: K slices of the out-projections (K = C) and of FF2 (K = F)
+  // when the [T][C] product has fewer output tiles than the GPU has CUs,
+  // and their fp32 partial products [slices][T][C]
+  int out_ksplit, ff2_ksplit;
+  float* res_ws;
 
   hipStream_t last_stream;
   unsigned timing_mask;
@@ -406,9 +412,29 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->attn_n_full = 0;
   b->attn_nsplit = 1;
   b->attn_part = nullptr;
+  b->out_ksplit = b->ff2_ksplit = 1;
+  b->res_ws = nullptr;
   if (b->bf16 && cr.ok()) {
     int cus = 0;
     cr.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    // The residual products write [T][C] in 128x128 tiles, two per CU.  With
+    // fewer tiles than CUs (short sequences), K is split into the most
+    // slices that keep every slice at least 1024 deep and all of them
+    // resident at once; the slices are summed in order by a second pass.
+    {
+      const long long tiles = ((T + 127) / 128) * ((C + 127) / 128);
+      auto slices = [&](int K) {
+        if (tiles >= cus) return 1;
+        for (int sp = 8; sp > 1; --sp)
+          if (K % (64 * sp) == 0 && K / sp >= 1024 && sp * tiles <= 2LL * cus) return sp;
+        return 1;
+      };
+      b->out_ksplit = slices(C);
+      b->ff2_ksplit = slices(b->F);
+      const int most = b->out_ksplit > b->ff2_ksplit ? b->out_ksplit : b->ff2_ksplit;
+      if (most > 1)
+        b->res_ws = static_cast<float*>(cr.alloc(sizeof(float) * most * T * C, "residual partial products"));
+    }
     if (const char* e = std::getenv("ST_ATTN_CUS")) cus = std::atoi(e);
     attention_bf16_plan(B, heads, b->N, b->N, cus, b->attn_n_full, b->attn_nsplit);
     if (b->attn_nsplit > 1) {
@@ -530,6 +556,12 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     p.epi.out_act = b->hcopy;
     p.epi.row_stats = b->hstats;
   };
+  // K slices of a residual product (bf16 path; set at create)
+  auto split_k = [&](GemmParams& p, int slices) {
+    if (!bf || slices <= 1) return;
+    p.ksplit = slices;
+    p.ws = b->res_ws;
+  };
   // h of the stage dump as fp32
   auto dump_h = [&]() {
     return bf ? f16_to_f32(b->hcopy, h_out, static_cast<long long>(T) * C, s)
@@ -608,6 +640,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              GemmParams p = gemm(b->o, C, L.wo1, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo1; p.epi.out_f32 = b->h; p.epi.ldo = C;
              keep_h(p);
+             split_k(p, b->out_ksplit);
              return G(p, ACT_BF16);
            }), "self-attention out-projection");
     ++stage;
@@ -653,6 +686,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              GemmParams p = gemm(b->o, C, L.wo2, C, T, C, C, EPI_RESID_F32);
              p.epi.bias = L.bo2; p.epi.out_f32 = b->h; p.epi.ldo = C;
              keep_h(p);
+             split_k(p, b->out_ksplit);
              return G(p, ACT_BF16);
            }), "cross-attention out-projection");
     ++stage;
@@ -679,6 +713,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              GemmParams p = gemm(b->f, F, L.w2, F, T, C, F, EPI_RESID_F32);
              p.epi.bias = L.b2; p.epi.out_f32 = b->h; p.epi.ldo = C;
              keep_h(p);
+             split_k(p, b->ff2_ksplit);
              return G(p, ACT_F16);
            }), "feed-forward 2");
     ++stage;

@@ -773,7 +773,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     wait_vmcnt_lds<0>();
     stage_barrier();
     if (k + 1 < nk) issue(k + 1, wa, wb);
-    else if (kPF) issue_res(wa, wb);
+    else if (kPF && p.ksplit <= 1) issue_res(wa, wb);
     steps(ca, cb);
   };
   for (int k = 0; k < nk; k += 2) {
@@ -843,6 +843,69 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   for (int z = 0; z < p.ksplit; ++z) acc += p.ws[z * mn + idx];
   const int row = static_cast<int>(idx / p.N);
   epi_store<EPI, bf16_t>(p.epi, row, static_cast<int>(idx - static_cast<long long>(row) * p.N), acc);
+}
+
+// Second pass of split-K for the fp16 stream (EPI_STORE_H16 / EPI_RESID_H16):
+// a thread takes 8 consecutive columns of one row, adds the slices in order,
+// then the bias (and the residual) and rounds to fp16 as the GEMM epilogue
+// does; the 8 threads of a 64-column block give its row sums.
+template <bool RES>
+__global__ __launch_bounds__(256) void splitk_reduce_h16_kernel(GemmParams p) {
+  const int cpr = p.N >> 3;  // threads per row (N % 64 == 0)
+  const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long row = g / cpr;
+  if (row >= p.M) return;  // whole 8-thread groups
+  const int c = static_cast<int>(g - row * cpr) * 8;
+  const long long mn = static_cast<long long>(p.M) * p.N;
+  const float* w = p.ws + row * p.N + c;
+  float v[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(w);
+    const float4 b = *reinterpret_cast<const float4*>(w + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  for (int z = 1; z < p.ksplit; ++z) {
+    const float4 a = *reinterpret_cast<const float4*>(w + z * mn);
+    const float4 b = *reinterpret_cast<const float4*>(w + z * mn + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  if (p.epi.bias) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] += p.epi.bias[c + k];
+  }
+  f16_t* h16 = static_cast<f16_t*>(p.epi.out_act) + row * p.epi.ldo + c;
+  if constexpr (RES) {
+    const uint4 hin = *reinterpret_cast<const uint4*>(h16);
+    const uint32_t hw[4] = {hin.x, hin.y, hin.z, hin.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x2 h2 = __builtin_bit_cast(f16x2, hw[k]);
+      v[2 * k] += static_cast<float>(h2[0]);
+      v[2 * k + 1] += static_cast<float>(h2[1]);
+    }
+  }
+  const uint4 o = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]), pack2h(v[4], v[5]),
+                             pack2h(v[6], v[7]));
+  *reinterpret_cast<uint4*>(h16) = o;
+  if (p.epi.row_stats) {
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x2 h2 = __builtin_bit_cast(f16x2, ow[k]);
+      v[2 * k] = static_cast<float>(h2[0]);
+      v[2 * k + 1] = static_cast<float>(h2[1]);
+    }
+    const float sum = row8_sum(((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+    const float mb = sum * (1.0f / 64.0f);
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q = fmaf(v[k] - mb, v[k] - mb, q);
+    const float m2 = row8_sum(q);
+    if ((threadIdx.x & 7) == 0)
+      p.epi.row_stats[row * (p.epi.ldo >> 6) + (c >> 6)] = make_float2(sum, m2);
+  }
 }
 
 // ---------------------------------------------------------------- fp32 GEMM
@@ -969,13 +1032,21 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
     return hipErrorInvalidValue;
   const int split = p.ksplit > 1 ? p.ksplit : 1;
   if (split > 1) {
-    if (!p.ws || p.K % (split * 64) || op != ACT_BF16 || p.epi.ln_stats || p.epi.row_stats ||
-        (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))
+    const bool h16 = p.epi.kind == EPI_STORE_H16 || p.epi.kind == EPI_RESID_H16;
+    if (!p.ws || p.K % (split * 64) || p.epi.ln_stats ||
+        (!h16 && (op != ACT_BF16 || p.epi.row_stats ||
+                  (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))))
       return hipErrorInvalidValue;
     // the slices (the kernel switches to the plain fp32 store), then the sum
     hipError_t e = launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, split, s);
     if (e != hipSuccess) return e;
     const long long mn = static_cast<long long>(p.M) * p.N;
+    if (h16) {
+      const unsigned blocks = static_cast<unsigned>((mn / 8 + 255) / 256);
+      if (p.epi.kind == EPI_RESID_H16) splitk_reduce_h16_kernel<true><<<blocks, 256, 0, s>>>(p);
+      else splitk_reduce_h16_kernel<false><<<blocks, 256, 0, s>>>(p);
+      return hipGetLastError();
+    }
     const unsigned blocks = static_cast<unsigned>((mn + 255) / 256);
     if (p.epi.kind == EPI_HEADS) splitk_reduce_kernel<EPI_HEADS><<<blocks, 256, 0, s>>>(p);
     else splitk_reduce_kernel<EPI_STORE_F32><<<blocks, 256, 0, s>>>(p);

@@ -90,9 +90,11 @@ struct GemmParams {
   long long ldb;
   int M, N, K;
   EpiParams epi;
-  // Split-K (gemm_mfma only): with ksplit > 1, K is cut into ksplit equal
-  // slices whose fp32 products land in ws[ksplit][M][N]; a second pass adds
-  // the slices in order and applies the epilogue element by element.
+  // Split-K (gemm_mfma only; EPI_HEADS or EPI_STORE_F32 with bf16 operands
+  // and no row sums, or EPI_STORE_H16 / EPI_RESID_H16; no folded LayerNorm):
+  // with ksplit > 1, K is cut into ksplit equal slices whose fp32 products
+  // land in ws[ksplit][M][N]; a second pass adds the slices in order and
+  // applies the epilogue.
   int ksplit;
   float* ws;
   // First output column this launch computes (set by gemm_mfma when it

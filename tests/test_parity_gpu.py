@@ -91,6 +91,9 @@ SMALL = [
     dict(name="b1_c64_1x1_d2", B=1, C=64, H=1, W=1, heads=1, D_ctx=64, depth=2),
     # C=320 (GEMM tiles ragged along N), 3 sublayers deep stack
     dict(name="b1_c320_12x12_d3", B=1, C=320, H=12, W=12, heads=5, D_ctx=768, depth=3),
+    # few output tiles and F=2048: FF2 split over K (bf16 storage), its row
+    # sums feeding the next layer's folded LayerNorm; ragged rows
+    dict(name="b1_c512_9x11_d2", B=1, C=512, H=9, W=11, heads=8, D_ctx=256, depth=2),
 ]
 
 
