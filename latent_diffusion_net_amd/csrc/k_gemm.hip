@@ -6,9 +6,10 @@
 // (WM*FM*32) x (WN*FN*32) outputs, each wavefront FM x FN MFMA blocks of
 // 32x32: 128x128 tiles of four 64x64 wavefronts (two workgroups per CU), or
 // 256x256 tiles of eight 128x64 wavefronts when the product has enough of
-// them.  K advances 64 at a time through two LDS stages filled by
-// buffer_load_dwordx4 ... lds (no staging registers), with one barrier per
-// stage; the LDS operand reads of each 16-wide K step are issued while the
+// them.  K advances 64 at a time through two LDS stages (four, with one
+// 128x128 workgroup per CU, when the product has no more tiles than CUs)
+// filled by buffer_load_dwordx4 ... lds (no staging registers), with one
+// barrier per stage; the LDS operand reads of each 16-wide K step are issued while the
 // MFMAs of the previous step run.  Each stage buffer is its own LDS object,
 // so the compiler can tell a DMA into one stage from reads of the other and
 // does not wait on it.  LDS rows are 128 bytes (64 elements, eight 16-byte
@@ -583,7 +584,7 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, uint16_t* ld
 // other buffers, then the four 16-wide K steps, the LDS operand reads of
 // step s+1 issued before the MFMAs of step s (two register sets; the
 // scheduling groups keep the compiler from folding them back into one).
-template <int EPI, typename OpT, int WM, int WN, int FM, int FN, int MINB, bool LN>
+template <int EPI, typename OpT, int WM, int WN, int FM, int FN, int MINB, bool LN, int NST>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
@@ -594,10 +595,17 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   static_assert(DPA * RPB * NW == TBM && DPB * RPB * NW == TBN, "DMA split");
   static_assert(FM % 2 == 0 && FN % 2 == 0, "epilogue works on 64x64 blocks");
   static_assert(2 * (TBM + TBN) * BKT * 2 >= NW * 16384, "epilogue staging");
+  static_assert(NST == 2 || (NST == 4 && TBM == 128 && NW == 4), "four stages: 128-row tiles");
+  // NST stage buffers per operand, each its own LDS object
+  constexpr int kXA = NST == 4 ? TBM * BKT : 8, kXB = NST == 4 ? TBN * BKT : 8;
   __shared__ __attribute__((aligned(16))) uint16_t sA0[TBM * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sA1[TBM * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[kXA];
+  __shared__ __attribute__((aligned(16))) uint16_t sA3[kXA];
   __shared__ __attribute__((aligned(16))) uint16_t sB0[TBN * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[TBN * BKT];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[kXB];
+  __shared__ __attribute__((aligned(16))) uint16_t sB3[kXB];
   // folded LayerNorm: (rstd, mean * rstd) per row and g per column
   __shared__ float2 ln_tab[LN ? TBM : 1];
   __shared__ __attribute__((aligned(16))) float ln_gtab[LN ? TBN : 4];
@@ -729,7 +737,22 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
         }
     }
   }
+  // Four-stage ring (NST == 4): every stage issues one DMA, unconditionally
+  // (past the last stage with an empty buffer range, which fetches nothing
+  // and zeroes buffers no later stage reads), so that every wait is the same
+  // partial count and no branch separates a DMA from the reads after it.
+  auto issue_at = [&](int k, bool valid, uint16_t* sa, uint16_t* sb) {
+    const int ab = valid ? abytes : 0, bb = valid ? bbytes : 0, so = valid ? k * BKT * 2 : 0;
+#pragma unroll
+    for (int j2 = 0; j2 < DPA; ++j2) dma16(A, ab, sa + (wave * DPA + j2) * 512, aoff[j2], so);
+#pragma unroll
+    for (int j2 = 0; j2 < DPB; ++j2) dma16(Bm, bb, sb + (wave * DPB + j2) * 512, boff[j2], so);
+  };
   issue(0, sA0, sB0);
+  if constexpr (NST == 4) {
+    issue_at(1, nk > 1, sA1, sB1);
+    issue_at(2, nk > 2, sA2, sB2);
+  }
   if constexpr (LN) {
     // the sums stay below the DMA issue (the empty statements take the
     // loaded values after it)
@@ -757,7 +780,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   // as zero), which land while the last stage computes; each wavefront then
   // takes its 64x64 part into registers before the buffers hold the
   // epilogue tiles.
-  constexpr bool kPF = EPI == EPI_RESID_H16 && WM == 2 && WN == 2 && FM == 2 && FN == 2;
+  constexpr bool kPF = EPI == EPI_RESID_H16 && WM == 2 && WN == 2 && FM == 2 && FN == 2 && NST == 2;
   auto issue_res = [&](uint16_t* wa, uint16_t* wb) {
     const long long lim = static_cast<long long>(M) * p.epi.ldo * 2;
 #pragma unroll
@@ -776,9 +799,34 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     else if (kPF && p.ksplit <= 1) issue_res(wa, wb);
     steps(ca, cb);
   };
-  for (int k = 0; k < nk; k += 2) {
-    stage(k, sA0, sB0, sA1, sB1);
-    if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
+  // Stage k of the four-stage ring waits until its own DMA has landed (the
+  // two issued after it may still be in flight), and after the barrier
+  // refills the buffers that stage k-1 read with stage k+3.
+  constexpr int kPer = DPA + DPB;  // DMA instructions per wavefront per stage
+  auto stage4 = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
+    wait_vmcnt_lds<2 * kPer>();
+    stage_barrier();
+    issue_at(k + 3, k + 3 < nk, wa, wb);
+    steps(ca, cb);
+  };
+  if constexpr (NST == 2) {
+    for (int k = 0; k < nk; k += 2) {
+      stage(k, sA0, sB0, sA1, sB1);
+      if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
+    }
+  } else {
+    int k = 0;
+    for (; k + 4 <= nk; k += 4) {
+      stage4(k, sA0, sB0, sA3, sB3);
+      stage4(k + 1, sA1, sB1, sA0, sB0);
+      stage4(k + 2, sA2, sB2, sA1, sB1);
+      stage4(k + 3, sA3, sB3, sA2, sB2);
+    }
+    const int rem = nk - k;
+    if (rem > 0) stage4(k, sA0, sB0, sA3, sB3);
+    if (rem > 1) stage4(k + 1, sA1, sB1, sA0, sB0);
+    if (rem > 2) stage4(k + 2, sA2, sB2, sA1, sB1);
+    wait_vmcnt_lds<0>();  // the empty DMAs past the last stage
   }
 
   uint4 resv[8];
@@ -798,7 +846,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   }
   // 16 KB per wavefront: the stage buffers taken in order
   float* stg_area;
-  {
+  if constexpr (NST == 4) {
+    // four 16 KB A buffers, one per wavefront
+    uint16_t* a = wave < 2 ? (wave == 0 ? sA0 : sA1) : (wave == 2 ? sA2 : sA3);
+    stg_area = reinterpret_cast<float*>(a);
+  } else {
     constexpr int PA = TBM * BKT * 2 / 16384;  // wavefront areas per A buffer
     constexpr int PB = TBN * BKT * 2 / 16384;
     int w = wave;
@@ -956,14 +1008,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 }  // namespace
 
 namespace {
-template <int WM, int WN, int FM, int FN, int MINB>
+template <int WM, int WN, int FM, int FN, int MINB, int NST = 2>
 hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStream_t s) {
   constexpr int TBM = WM * FM * 32, TBN = WN * FN * 32;
   const dim3 grid(((p.M + TBM - 1) / TBM) * ((p.N - p.n_off + TBN - 1) / TBN) * split);
   constexpr int threads = 64 * WM * WN;
 #define ST_PIPE_LAUNCH(E, LN)                                                                          \
-  if (op == ACT_F16) gemm_pipe_kernel<E, f16_t, WM, WN, FM, FN, MINB, LN><<<grid, threads, 0, s>>>(p); \
-  else gemm_pipe_kernel<E, bf16_t, WM, WN, FM, FN, MINB, LN><<<grid, threads, 0, s>>>(p);
+  if (op == ACT_F16) gemm_pipe_kernel<E, f16_t, WM, WN, FM, FN, MINB, LN, NST><<<grid, threads, 0, s>>>(p); \
+  else gemm_pipe_kernel<E, bf16_t, WM, WN, FM, FN, MINB, LN, NST><<<grid, threads, 0, s>>>(p);
   const bool ln = p.epi.ln_stats != nullptr;
   switch (kind) {
     case EPI_STORE_F32: ST_PIPE_LAUNCH(EPI_STORE_F32, false) break;
@@ -1056,12 +1108,17 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   // them to give most CUs one; otherwise 128x128 tiles, two per CU.
   const int mtb = (p.M + 255) / 256, ntb = (p.N + 255) / 256;
   const long long big_tiles = static_cast<long long>(mtb) * ntb;
-  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN)
+  const int cus = cu_count();
+  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN) {
+    // 128x128 tiles: with no more of them than CUs, one per CU with a
+    // four-stage ring (128 KB of LDS), else two per CU with two stages
+    const long long tiles = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128);
+    if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 4>(p, op, p.epi.kind, 1, s);
     return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
+  }
   // When the last round of large tiles would leave more than a quarter of
   // the CUs idle, the columns of whole rounds take large tiles and the rest
   // 128x128 tiles (two per CU) in a second launch.
-  const int cus = cu_count();
   const long long rounds = big_tiles / cus, tail = big_tiles % cus;
   const int nb = rounds > 0 ? static_cast<int>(rounds * cus / mtb) : 0;
   if (tail > 0 && 4 * tail < 3LL * cus && nb >= 1 && nb < ntb) {
