@@ -1109,13 +1109,14 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   const int mtb = (p.M + 255) / 256, ntb = (p.N + 255) / 256;
   const long long big_tiles = static_cast<long long>(mtb) * ntb;
   const int cus = cu_count();
-  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN) {
-    // 128x128 tiles: with no more of them than CUs, one per CU with a
-    // four-stage ring (128 KB of LDS), else two per CU with two stages
-    const long long tiles = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128);
-    if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 4>(p, op, p.epi.kind, 1, s);
-    return launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, 1, s);
-  }
+  // 128x128 tiles: with no more of them than CUs, one per CU with a
+  // four-stage ring (128 KB of LDS), else two per CU with two stages
+  auto small_tiles = [&](const GemmParams& q) {
+    const long long tiles = static_cast<long long>((q.M + 127) / 128) * ((q.N - q.n_off + 127) / 128);
+    if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 4>(q, op, q.epi.kind, 1, s);
+    return launch_pipe<2, 2, 2, 2, 2>(q, op, q.epi.kind, 1, s);
+  };
+  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN) return small_tiles(p);
   // When the last round of large tiles would leave more than a quarter of
   // the CUs idle, the columns of whole rounds take large tiles and the rest
   // 128x128 tiles (two per CU) in a second launch.
@@ -1128,7 +1129,7 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
     if (e != hipSuccess) return e;
     q.N = p.N;
     q.n_off = nb * 256;
-    return launch_pipe<2, 2, 2, 2, 2>(q, op, p.epi.kind, 1, s);
+    return small_tiles(q);
   }
   return launch_pipe<2, 4, 4, 2, 1>(p, op, p.epi.kind, 1, s);
 }
