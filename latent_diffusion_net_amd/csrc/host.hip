@@ -398,9 +398,13 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
     const int ctx_rows = B * ST_CTX_LEN;
     const long long tiles = ((ctx_rows + 127) / 128) * ((kvrows + 127) / 128);
     b->ctx_ksplit = 1;
-    if (b->bf16 && tiles < 128)
+    int cus = 0;
+    if (b->bf16 && tiles < 128) {
+      cr.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+      // the most slices (up to 8) whose workgroups all fit one per CU
       for (int sp = 8; sp > 1; sp /= 2)
-        if (D_ctx % (sp * 64) == 0) { b->ctx_ksplit = sp; break; }
+        if (D_ctx % (sp * 64) == 0 && tiles * sp <= cus) { b->ctx_ksplit = sp; break; }
+    }
     b->ctx_ws = b->ctx_ksplit > 1
                     ? static_cast<float*>(cr.alloc(sizeof(float) * b->ctx_ksplit * ctx_rows * kvrows,
                                                    "context K/V partial products"))

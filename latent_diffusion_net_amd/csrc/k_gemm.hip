@@ -1089,8 +1089,11 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
         (!h16 && (op != ACT_BF16 || p.epi.row_stats ||
                   (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))))
       return hipErrorInvalidValue;
-    // the slices (the kernel switches to the plain fp32 store), then the sum
-    hipError_t e = launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, split, s);
+    // the slices (the kernel switches to the plain fp32 store; one 128x128
+    // workgroup per CU with four stages when they all fit so), then the sum
+    const long long slice_wgs = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128) * split;
+    hipError_t e = slice_wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 4>(p, op, p.epi.kind, split, s)
+                                           : launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, split, s);
     if (e != hipSuccess) return e;
     const long long mn = static_cast<long long>(p.M) * p.N;
     if (h16) {
