@@ -104,6 +104,11 @@ typedef struct {
  *           synchronises it before returning.
  *   out:    receives the handle; set to NULL on any error.
  * Returns ST_OK, or an error with nothing allocated.
+ * Environment, read here: ST_MAX_DEVICE_BYTES (decimal) caps the device
+ * memory the handle may allocate (beyond it create fails with
+ * ST_ERR_OUT_OF_MEMORY); ST_ATTN_CUS overrides the CU count that the bf16
+ * self-attention's load-balance plan assumes (it changes only how the work
+ * is split, not the result beyond rounding order; for tests).
  */
 st_status st_block_create(int B, int C, int H, int W, int heads, int D_ctx,
                           int depth, st_dtype dtype, const st_block_weights *w,
