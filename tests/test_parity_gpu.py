@@ -222,6 +222,38 @@ def test_forward_rejects_aliasing_on_device():
     blk.close()
 
 
+def test_create_respects_device_memory_cap(monkeypatch):
+    """ST_MAX_DEVICE_BYTES (read at create): a handle that needs more device
+    memory is refused with ST_ERR_OUT_OF_MEMORY and keeps nothing; a cap
+    above the need changes nothing (bitwise)."""
+    import torch
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    from latent_diffusion_net_amd.binding import ST_ERR_OUT_OF_MEMORY, STError
+    cfg = synth.BlockConfig("cap", dtype="bf16", B=1, C=64, H=8, W=8, heads=1, D_ctx=64, depth=1)
+    inp = synth.make_inputs(cfg, 31)
+    _say("[gpu] device memory cap")
+    p = params_to_device(inp["params"], "bf16")
+    x = array_to_device(inp["x"], "bf16")
+    ctx = array_to_device(inp["ctx"], "bf16")
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    y0 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    blk.close()
+    free0, _ = torch.cuda.mem_get_info()
+    monkeypatch.setenv("ST_MAX_DEVICE_BYTES", "65536")
+    with pytest.raises(STError) as e:
+        STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    assert e.value.status == ST_ERR_OUT_OF_MEMORY
+    free1, _ = torch.cuda.mem_get_info()
+    assert abs(free1 - free0) <= 4 << 20, (free0, free1)
+    monkeypatch.setenv("ST_MAX_DEVICE_BYTES", str(1 << 40))
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    y1 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    blk.close()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
 @pytest.mark.parametrize("cus,spec", [
     # 32 query tiles over 12 CUs: 24 whole, 8 split in 2 over 64 key tiles
     (12, dict(name="split2", B=1, C=64, H=64, W=64, heads=1, D_ctx=64, depth=1)),
