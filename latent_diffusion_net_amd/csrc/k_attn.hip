@@ -23,6 +23,7 @@
 //
 // fp32 path (debug builds): one thread per query row, K/V tiles in LDS,
 // online softmax in fp32.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -578,18 +579,19 @@ void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full,
   nsplit = sp;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; host threads may
+// race to fill an entry, with the same value).
 static int attn_cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {

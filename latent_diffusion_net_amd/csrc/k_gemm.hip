@@ -24,6 +24,7 @@
 //
 // fp32 path (debug builds of the block): a plain LDS-tiled fp32 FMA GEMM with
 // the same epilogues.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1044,18 +1045,19 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
 }
 }  // namespace
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; host threads may
+// race to fill an entry, with the same value).
 static int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
