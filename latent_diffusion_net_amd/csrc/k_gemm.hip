@@ -1076,8 +1076,9 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
                           (p.epi.kind != EPI_STORE_F32 && p.epi.kind != EPI_RESID_F32 &&
                            p.epi.kind != EPI_STORE_H16 && p.epi.kind != EPI_RESID_H16)))
     return hipErrorInvalidValue;
+  // fp16 stream rows move as 16-byte vectors
   if ((p.epi.kind == EPI_STORE_H16 || p.epi.kind == EPI_RESID_H16) &&
-      (!p.epi.out_act || p.N % 64 || p.epi.ldo % 4))
+      (!p.epi.out_act || p.N % 64 || p.epi.ldo % 8))
     return hipErrorInvalidValue;
   if (p.K % 64) return hipErrorInvalidValue;
   // the DMA addresses each operand with 32-bit byte offsets
