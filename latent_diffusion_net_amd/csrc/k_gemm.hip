@@ -136,18 +136,30 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
     bj[j] = p.epi.bias ? p.epi.bias[C0 + j * 32 + l32] : 0.f;
     if constexpr (LN) gj[j] = ln_cols[j * 32 + l32];
   }
+  // rows come in runs of four (r % 4): their (rstd, mean * rstd) pairs are
+  // read as two 16-byte words before the run's stores
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-      float2 k = make_float2(1.f, 0.f);
-      if constexpr (LN) k = ln_rows[lr];
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int lr0 = i * 32 + 8 * g4 + 4 * lhi;
+      float2 k[4] = {make_float2(1.f, 0.f), make_float2(1.f, 0.f), make_float2(1.f, 0.f),
+                     make_float2(1.f, 0.f)};
+      if constexpr (LN) {
+        const float4 u = *reinterpret_cast<const float4*>(ln_rows + lr0);
+        const float4 w = *reinterpret_cast<const float4*>(ln_rows + lr0 + 2);
+        k[0] = make_float2(u.x, u.y); k[1] = make_float2(u.z, u.w);
+        k[2] = make_float2(w.x, w.y); k[3] = make_float2(w.z, w.w);
+      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float v = acc[i][j][r];
-        if constexpr (LN) v = fmaf(v, k.x, -k.y * gj[j]);
-        stage[stg(lr, j * 32 + l32)] = (v + bj[j]) * ca.scale;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * g4 + jj;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float v = acc[i][j][r];
+          if constexpr (LN) v = fmaf(v, k[jj].x, -k[jj].y * gj[j]);
+          stage[stg(lr0 + jj, j * 32 + l32)] = (v + bj[j]) * ca.scale;
+        }
       }
     }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
@@ -608,7 +620,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   __shared__ __attribute__((aligned(16))) uint16_t sB2[kXB];
   __shared__ __attribute__((aligned(16))) uint16_t sB3[kXB];
   // folded LayerNorm: (rstd, mean * rstd) per row and g per column
-  __shared__ float2 ln_tab[LN ? TBM : 1];
+  __shared__ __attribute__((aligned(16))) float2 ln_tab[LN ? TBM : 2];
   __shared__ __attribute__((aligned(16))) float ln_gtab[LN ? TBN : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
