@@ -134,9 +134,16 @@ def test_sharp_softmax(dtype, grid):
     assert rel_l2(y, yo) <= (1e-2 if dtype == "bf16" else 1e-5)
 
 
-def test_stages_bf16():
+@pytest.mark.parametrize("shape", [
+    (2, 128, 15, 15, 2, 128),
+    # F = 2048 over few output tiles: FF2 takes the split-K path, so the
+    # stream after each feed-forward comes from the ordered slice sum
+    (1, 512, 9, 11, 8, 256),
+], ids=["b2_c128", "b1_c512_splitk"])
+def test_stages_bf16(shape):
     """Residual stream after proj_in and after every sublayer."""
-    cfg = synth.BlockConfig("stages", 2, 128, 15, 15, 2, 128, 2, "bf16")
+    B, C, H, W, heads, D_ctx = shape
+    cfg = synth.BlockConfig("stages", B, C, H, W, heads, D_ctx, 2, "bf16")
     inp = synth.make_inputs(cfg, 9, bias_std=0.05, norm_std=0.2)
     _, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
                                 intermediates=True)
