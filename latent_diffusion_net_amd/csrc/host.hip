@@ -421,16 +421,17 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   if (b->bf16 && cr.ok()) {
     int cus = 0;
     cr.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
-    // The residual products write [T][C] in 128x128 tiles, two per CU.  With
-    // fewer tiles than CUs (short sequences), K is split into the most
-    // slices that keep every slice at least 1024 deep and all of them
-    // resident at once; the slices are summed in order by a second pass.
+    // The residual products write [T][C] in 128x128 tiles.  With fewer
+    // tiles than CUs (short sequences) each tile has a CU to itself on the
+    // four-stage ring, and K is split into the most slices that keep every
+    // slice at least 1024 deep and still give each slice a CU of its own;
+    // the slices are summed in order by a second pass.
     {
       const long long tiles = ((T + 127) / 128) * ((C + 127) / 128);
       auto slices = [&](int K) {
         if (tiles >= cus) return 1;
         for (int sp = 8; sp > 1; --sp)
-          if (K % (64 * sp) == 0 && K / sp >= 1024 && sp * tiles <= 2LL * cus) return sp;
+          if (K % (64 * sp) == 0 && K / sp >= 1024 && sp * tiles <= cus) return sp;
         return 1;
       };
       b->out_ksplit = slices(C);
