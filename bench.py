@@ -6,11 +6,14 @@ the SDXL Down1 workload: B=2, C=640, 64x64 latent (4096 tokens per sample),
 10 heads of 64, context [2, 77, 2048], depth 2, bf16 storage, seeded
 random-init weights (N(0, 0.02^2)) and N(0, 1) inputs already resident in HBM.
 
-Prints one JSON line: block tokens/s as `value`, the self-attention kernel's
-achieved TFLOP/s against the bf16 MFMA peak as `roofline` (its duration from
-HIP events recorded by the library around each self-attention launch, on the
-stream it runs on, during the timed region), and the fp64 CPU oracle timed on
-the host as `cpu_baseline`.
+Prints one JSON line: block tokens/s as `value` (wall clock over the timed
+steps), the median and minimum of the same forwards each bracketed by its
+own pair of HIP events, the self-attention kernel's achieved TFLOP/s against
+the bf16 MFMA peak as `roofline` (its duration from HIP events recorded by
+the library around each self-attention launch, on the stream it runs on,
+during the timed region: mean, median and minimum per launch), the same rate
+against a measured MFMA-loop ceiling with the shader clock observed during
+that loop, and the fp64 CPU oracle timed on the host as `cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -19,7 +22,9 @@ import csv
 import hashlib
 import json
 import os
+import platform
 import re
+import statistics
 import sys
 import time
 
@@ -59,6 +64,11 @@ def block_flops(cfg) -> float:
 # cross Q and FF1), so their row is absent and their cost sits in those rows;
 # likewise the cross-attention when it runs in the cross Q epilogue (its
 # time is in A8, whose rate is still computed on the projection's flops).
+def fused_cross(cfg) -> bool:
+    """The cross-attention runs in the epilogue of its Q projection."""
+    return getattr(cfg, "dtype", "bf16") == "bf16" and cfg.N % 64 == 0
+
+
 def row_work(cfg):
     T, C, B, N, D, F, h = cfg.T, cfg.C, cfg.B, cfg.N, cfg.D_ctx, cfg.F, cfg.heads
     return {
@@ -68,8 +78,15 @@ def row_work(cfg):
         "qkv": ("A4 Q/K/V projection", "mfma", 6.0 * T * C * C),
         "self_attn": ("A5 self-attention", "mfma", attention_flops(cfg)),
         "attn_out": ("A6/A11 out-projections + residual", "mfma", 2.0 * T * C * C),
-        "cross_q": ("A8 cross-attention Q", "mfma", 2.0 * T * C * C),
-        "ctx_kv": ("A9 context K/V (all layers)", "mfma", 2.0 * B * 77 * 2 * C * cfg.depth * D),
+        # with the cross-attention in its epilogue (bf16, H*W % 64 == 0) the
+        # launch also does the 77-key attention: QK^T and PV flops counted
+        "cross_q": ("A8 cross-attention Q", "mfma",
+                    2.0 * T * C * C + (4.0 * B * N * 77 * C if fused_cross(cfg) else 0.0)),
+        # B*77 rows: 154 flop/B at most, below the ridge (about 312 flop/B at
+        # 2.5 PFLOP/s and 8 TB/s): rated on its bytes -- the weights of all
+        # layers, the context and the K/V it writes, each moved once
+        "ctx_kv": ("A9 context K/V (all layers)", "hbm",
+                   2.0 * (2 * C * cfg.depth * D + B * 77 * D + 2 * B * 77 * C * cfg.depth)),
         "cross_attn": ("A10 cross-attention", "hbm", 2.0 * T * C * 2 + 2.0 * B * h * 77 * 64 * 2),
         "ff1_geglu": ("A13 FF1 + GEGLU", "mfma", 16.0 * T * C * C),
         "ff2": ("A14 FF2 + residual", "mfma", 8.0 * T * C * C),
@@ -171,13 +188,26 @@ def summarize_pmc(fetch_csv, write_csv):
             "fetch_bytes": fetch_b, "write_bytes": write_b}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, inp):
     """The fp64 oracle as it stands: one full forward of the same workload."""
     import oracle.block as ob
-    threads = None
+    threads, blas = None, "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max((p.get("num_threads") or 0) for p in info) or None
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '?')}"
     except Exception:
         pass
     t0 = time.perf_counter()
@@ -185,6 +215,8 @@ def cpu_baseline(cfg, inp):
     dt = time.perf_counter() - t0
     return {"value": cfg.T / dt, "unit": "tokens/s",
             "cores": threads or os.cpu_count(), "kind": "oracle",
+            "cpu": cpu_model(), "blas": blas,
+            "fp64_gflops": round(block_flops(cfg) / dt / 1e9, 2),
             "sample": f"one full fp64 forward of the same workload ({cfg.T} tokens), {dt:.1f} s"}
 
 
@@ -247,20 +279,26 @@ def main():
         return
     blk.read_timing()
     blk.set_timing(["self_attn"])
+    # one event pair around each forward, on the stream the forward runs on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i][0].record(stream)
         blk.forward(x, ctx, y, stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    timing = blk.read_timing()
+    launches = blk.read_timing_launches()
     blk.set_timing([])
 
+    fwd_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = dt * 1e3 / args.steps
     tokens_per_s = cfg.T / (dt / args.steps)
-    attn = timing.get("self_attn", {"ms": float("nan"), "launches": 1})
-    attn_s = attn["ms"] / 1e3 / attn["launches"]
+    attn_ms = [ms for k, ms in launches if k == "self_attn"] or [float("nan")]
+    attn_s = statistics.fmean(attn_ms) / 1e3
     attn_tflops = attention_flops(cfg) / attn_s / 1e12
 
     # Every kernel kind against its roofline, from a few more forwards after
@@ -277,6 +315,10 @@ def main():
     blk.close()
     copy_gbs = copy_ceiling_gbs(torch, dev)
     rows = row_rates(cfg, kt, copy_gbs)
+    from latent_diffusion_net_amd.binding import measure_mfma_bf16
+    mfma_tflops, sclk = measure_mfma_bf16(stream=stream)
+    attn_med_s = statistics.median(attn_ms) / 1e3
+    attn_min_s = min(attn_ms) / 1e3
 
     result = {
         "metric": METRIC,
@@ -300,7 +342,17 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel (self-attention)",
                      "us_per_launch": attn_s * 1e6,
-                     "flops_per_launch": attention_flops(cfg)},
+                     "us_per_launch_median": attn_med_s * 1e6,
+                     "us_per_launch_min": attn_min_s * 1e6,
+                     "launches_timed": len(attn_ms),
+                     "achieved_median": attention_flops(cfg) / attn_med_s / 1e12,
+                     "flops_per_launch": attention_flops(cfg),
+                     "measured_mfma_ceiling_tflops": round(mfma_tflops, 1),
+                     "frac_of_measured_ceiling": attn_tflops / mfma_tflops,
+                     "sclk_mhz_during_ceiling": round(sclk, 1)},
+        "forward_ms": {"median": statistics.median(fwd_ms), "min": min(fwd_ms),
+                       "mean": statistics.fmean(fwd_ms), "timed_by": "HIP events, one pair per forward"},
+        "tokens_per_s_median_forward": cfg.T / (statistics.median(fwd_ms) * 1e-3),
         "block_tflops": block_flops(cfg) / (dt / args.steps) / 1e12,
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "rows": rows,

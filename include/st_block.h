@@ -32,13 +32,22 @@
  * encoding; dropout is the identity.
  *
  * Precision.  ST_DTYPE_BF16: inputs, weights and output are bf16; GEMM and
- * attention operands are bf16 with fp32 accumulation; norm statistics,
- * softmax and the residual stream h are fp32.  ST_DTYPE_F32: every buffer and
- * every operation is fp32 (a debug path for tight parity checks).
+ * attention operands are 16-bit (fp16 where a normalised activation or the
+ * GEGLU output meets a weight, bf16 for attention and the context) with fp32
+ * accumulation; norm statistics and the softmax are fp32; the residual
+ * stream h is kept in fp16.  Every fp16 intermediate (h, the GEGLU output,
+ * the GroupNorm output) is range-checked where it is stored: a value that
+ * leaves the fp16 range (|v| >= 65520, or NaN) sets a flag of the handle,
+ * which st_block_check_range() reports -- a forward never hides such an
+ * overflow.  ST_DTYPE_F32: every buffer and every operation is fp32 (a
+ * debug path for tight parity checks).
  *
  * Threading.  Distinct handles are independent.  One handle runs one forward
- * at a time: two forwards on one handle that overlap on the device race on
- * its workspace.  st_last_error() is per host thread.
+ * at a time: forwards (and forward_stage calls) on one handle must be
+ * serialised by the caller -- two that overlap on the device race on the
+ * handle's workspace (and its range flag), e.g. when enqueued on two
+ * streams without an event between them.  st_last_error() is per host
+ * thread.
  */
 #ifndef ST_BLOCK_H
 #define ST_BLOCK_H
@@ -58,7 +67,9 @@ typedef enum {
   ST_ERR_INVALID = 1,       /* bad argument: NULL, shape, alignment, aliasing */
   ST_ERR_UNSUPPORTED = 2,   /* valid shape the kernels cannot compute */
   ST_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
-  ST_ERR_DEVICE = 4         /* a HIP call failed; st_last_error() has the text */
+  ST_ERR_DEVICE = 4,        /* a HIP call failed; st_last_error() has the text */
+  ST_ERR_RANGE = 5          /* an fp16 intermediate left the fp16 range
+                               (st_block_check_range) */
 } st_status;
 
 typedef enum { ST_DTYPE_BF16 = 0, ST_DTYPE_F32 = 1 } st_dtype;
@@ -94,8 +105,13 @@ typedef struct {
 /*
  * Create a block handle on the current HIP device.
  *   B, H, W >= 1; C % 64 == 0 and heads * 64 == C; D_ctx % 64 == 0, D_ctx >= 64;
- *   depth >= 1; dtype one of st_dtype.  B*H*W*C and every workspace size must
- *   fit the device.
+ *   depth >= 1; dtype one of st_dtype.  Every workspace must fit the device.
+ *   The kernels address each GEMM operand with 32-bit byte offsets, so
+ *   shapes whose largest operands reach 2^31 bytes are refused with
+ *   ST_ERR_UNSUPPORTED: B*H*W*4*C >= 2^30 (the GEGLU output), 16*C*C >= 2^31
+ *   (the FF1 weights) or 4*C*depth*D_ctx >= 2^31 (the context K/V weights
+ *   of all layers).  A handle that create returns therefore never fails a
+ *   forward on its shape.
  *   w:      device pointers as described above; every non-bias weight must be
  *           non-NULL and 16-byte aligned.  The weights are COPIED (and
  *           repacked) into memory the handle owns; the caller may free them
@@ -121,7 +137,11 @@ st_status st_block_create(int B, int C, int H, int W, int heads, int D_ctx,
  *   y   [B][C][H][W]      device, dtype, 16-byte aligned, written
  * y must not overlap x or ctx.  The call only enqueues work and returns before
  * it completes; x, ctx and y must stay valid until the stream reaches it.
- * It allocates nothing.  On an error nothing is enqueued.
+ * It allocates nothing.  Every argument is validated before the first
+ * launch: on ST_ERR_INVALID nothing is enqueued.  ST_ERR_DEVICE (a launch
+ * that the HIP runtime refused) can leave earlier launches of the same call
+ * enqueued; y is then undefined.  Forwards on one handle must not overlap
+ * (see Threading).
  */
 st_status st_block_forward(st_block *blk, const void *x, const void *ctx,
                            void *y, void *stream);
@@ -136,8 +156,25 @@ st_status st_block_forward(st_block *blk, const void *x, const void *ctx,
 st_status st_block_forward_stage(st_block *blk, const void *x, const void *ctx,
                                  int stage, float *h_out, void *stream);
 
-/* Synchronise the handle's last stream and free everything.  NULL-safe. */
+/*
+ * Wait for the handle's device to go idle (every stream any forward used,
+ * including streams the caller may have destroyed since), then free
+ * everything.  NULL-safe.
+ */
 void st_block_destroy(st_block *blk);
+
+/*
+ * Range check of the fp16 intermediates (bf16 storage).  Enqueues a read of
+ * the handle's range flag on `stream`, waits for it, and returns
+ * ST_ERR_RANGE (and clears the flag) if any forward on this handle since the
+ * last check stored a value outside the fp16 range -- the residual stream
+ * h, the GEGLU output or the GroupNorm output reached |v| >= 65520 or NaN;
+ * the y of those forwards is then not valid.  ST_OK otherwise, and always
+ * for fp32 storage.  Call it on the stream of the forwards (or after they
+ * are complete); like a forward, it must not overlap another call on the
+ * same handle.
+ */
+st_status st_block_check_range(st_block *blk, void *stream);
 
 /* Text of the last error on this host thread; never NULL ("" if none). */
 const char *st_last_error(void);
@@ -180,6 +217,27 @@ typedef struct {
 
 st_status st_block_set_timing(st_block *blk, unsigned kind_mask);
 st_status st_block_read_timing(st_block *blk, st_timing *out);
+
+/*
+ * The same recorded launches one by one, in launch order: kinds[i] (an
+ * st_kernel_kind) and ms[i] for the first `capacity` of them; *count
+ * receives the number recorded.  Clears them, as st_block_read_timing does.
+ */
+st_status st_block_read_timing_launches(st_block *blk, int *kinds, double *ms,
+                                        long long capacity, long long *count);
+
+/*
+ * Measurement helper: the sustained bf16 MFMA rate of the current device.
+ * Launches a kernel of two workgroups per CU whose wavefronts each run four
+ * independent v_mfma_f32_32x32x16_bf16 chains for `iters` rounds (no memory
+ * traffic in the loop), timed by HIP events on `stream` (after one untimed
+ * launch), and reads the shader-cycle and real-time counters around each
+ * workgroup's loop.  *tflops = dense bf16 TFLOP/s achieved; *sclk_mhz = the
+ * mean shader clock during the loop.  Allocates and frees a small buffer;
+ * synchronises `stream`.
+ */
+st_status st_measure_mfma_bf16(int iters, void *stream, double *tflops,
+                               double *sclk_mhz);
 
 #ifdef __cplusplus
 }

@@ -14,10 +14,11 @@ from typing import Dict, Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libst_block.so")
 
-ST_OK, ST_ERR_INVALID, ST_ERR_UNSUPPORTED, ST_ERR_OUT_OF_MEMORY, ST_ERR_DEVICE = range(5)
+(ST_OK, ST_ERR_INVALID, ST_ERR_UNSUPPORTED, ST_ERR_OUT_OF_MEMORY, ST_ERR_DEVICE,
+ ST_ERR_RANGE) = range(6)
 ST_DTYPE_BF16, ST_DTYPE_F32 = 0, 1
 STATUS_NAMES = {0: "ST_OK", 1: "ST_ERR_INVALID", 2: "ST_ERR_UNSUPPORTED",
-                3: "ST_ERR_OUT_OF_MEMORY", 4: "ST_ERR_DEVICE"}
+                3: "ST_ERR_OUT_OF_MEMORY", 4: "ST_ERR_DEVICE", 5: "ST_ERR_RANGE"}
 
 KERNEL_KINDS = ("gn_stats", "proj_in", "layernorm", "qkv", "self_attn",
                 "attn_out", "cross_q", "ctx_kv", "cross_attn", "ff1_geglu",
@@ -33,8 +34,9 @@ BLOCK_FIELDS = ("gn_w", "gn_b", "proj_in_w", "proj_in_b", "proj_out_w",
 
 # Every function include/st_block.h declares.
 EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_stage",
-           "st_block_destroy", "st_last_error", "st_block_set_timing",
-           "st_block_read_timing")
+           "st_block_destroy", "st_block_check_range", "st_last_error",
+           "st_block_set_timing", "st_block_read_timing",
+           "st_block_read_timing_launches", "st_measure_mfma_bf16")
 
 
 class LayerWeights(ctypes.Structure):
@@ -93,6 +95,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_block_set_timing.restype = i
     lib.st_block_read_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.st_block_read_timing.restype = i
+    ll, dbl = ctypes.c_longlong, ctypes.c_double
+    lib.st_block_check_range.argtypes = [vp, vp]
+    lib.st_block_check_range.restype = i
+    lib.st_block_read_timing_launches.argtypes = [vp, ctypes.POINTER(i), ctypes.POINTER(dbl),
+                                                  ll, ctypes.POINTER(ll)]
+    lib.st_block_read_timing_launches.restype = i
+    lib.st_measure_mfma_bf16.argtypes = [i, vp, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    lib.st_measure_mfma_bf16.restype = i
     _lib = lib
     return lib
 
@@ -187,6 +197,20 @@ class STBlock:
         return {k: {"ms": t.ms[i], "launches": t.launches[i]}
                 for i, k in enumerate(KERNEL_KINDS) if t.launches[i]}
 
+    def check_range(self, stream=None):
+        """Raise STError(ST_ERR_RANGE) if an fp16 intermediate of a forward
+        since the last check left the fp16 range (waits for ``stream``)."""
+        _check(self._lib.st_block_check_range(self._h, _stream_handle(stream)))
+
+    def read_timing_launches(self, capacity: int = 4096):
+        """[(kind name, ms)] of every recorded launch, in launch order."""
+        kinds = (ctypes.c_int * capacity)()
+        ms = (ctypes.c_double * capacity)()
+        n = ctypes.c_longlong()
+        _check(self._lib.st_block_read_timing_launches(self._h, kinds, ms, capacity,
+                                                       ctypes.byref(n)))
+        return [(KERNEL_KINDS[kinds[i]], ms[i]) for i in range(min(n.value, capacity))]
+
     def close(self):
         if self._h is not None:
             self._lib.st_block_destroy(self._h)
@@ -197,6 +221,15 @@ class STBlock:
             self.close()
         except Exception:
             pass
+
+
+def measure_mfma_bf16(iters: int = 16384, stream=None):
+    """(TFLOP/s, shader MHz) of a dense bf16 MFMA loop on the current device."""
+    lib = load_library()
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+    _check(lib.st_measure_mfma_bf16(iters, _stream_handle(stream), ctypes.byref(tf),
+                                    ctypes.byref(mhz)))
+    return tf.value, mhz.value
 
 
 def params_to_device(params: Dict, dtype: str, device="cuda"):

@@ -126,6 +126,16 @@ __device__ __forceinline__ floatx16 mfma32x32x16(const uint4& a, const uint4& b,
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// True when one of the fp16 values packed in the dwords is infinite or NaN
+// (exponent field all ones).
+__device__ __forceinline__ bool f16_pair_nonfinite(uint32_t d) {
+  return ((d & 0x7c00u) == 0x7c00u) | ((d & 0x7c000000u) == 0x7c000000u);
+}
+__device__ __forceinline__ bool f16x8_nonfinite(const uint4& w) {
+  return f16_pair_nonfinite(w.x) | f16_pair_nonfinite(w.y) | f16_pair_nonfinite(w.z) |
+         f16_pair_nonfinite(w.w);
+}
+
 // s_waitcnt that waits for vmcnt <= n and for every LDS access of this
 // wavefront (lgkmcnt 0), expcnt left at its maximum.
 template <int N>

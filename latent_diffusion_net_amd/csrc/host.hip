@@ -128,8 +128,11 @@ struct st_block {
   // and their fp32 partial products [slices][T][C]
   int out_ksplit, ff2_ksplit;
   float* res_ws;
+  // bf16 path: set to 1 by a kernel that stores a non-finite fp16 value
+  // (the residual stream, the GEGLU output or the normalised input); read
+  // and cleared by st_block_check_range
+  int* range_flag;
 
-  hipStream_t last_stream;
   unsigned timing_mask;
   std::vector<PendingTiming> pending;
   std::vector<hipEvent_t> spare_events;
@@ -238,10 +241,18 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   if (dtype != ST_DTYPE_BF16 && dtype != ST_DTYPE_F32) return fail(ST_ERR_INVALID, "unknown dtype");
   const long long N = static_cast<long long>(H) * W;
   const long long T = N * B;
-  // Kernels index activations with 32-bit element offsets: the largest
-  // buffer, the GEGLU output [T][4C], must stay below 2^31 elements.
-  if (N > (1LL << 24) || T * 4LL * C >= (1LL << 31))
-    return fail(ST_ERR_UNSUPPORTED, "B*H*W*4*C must stay below 2^31");
+  // The GEMMs address each operand through a buffer resource with 32-bit
+  // byte offsets: every operand must stay below 2^31 bytes.  The largest
+  // are the GEGLU output [T][4C] (FF2's A operand), the FF1 weights
+  // [8C][C] and the context K/V weights of all layers [2C*depth][D_ctx]
+  // (16-bit on the bf16 path; the fp32 path shares the limits).
+  if (N > (1LL << 24) || T * 4LL * C * 2 >= (1LL << 31))
+    return fail(ST_ERR_UNSUPPORTED, "B*H*W*4*C must stay below 2^30 (FF2 operand of 2^31 bytes)");
+  if (16LL * C * C >= (1LL << 31))
+    return fail(ST_ERR_UNSUPPORTED, "C too large: the FF1 weights [8C][C] reach 2^31 bytes");
+  if (4LL * C * depth * D_ctx >= (1LL << 31) || 2LL * B * ST_CTX_LEN * D_ctx >= (1LL << 31))
+    return fail(ST_ERR_UNSUPPORTED,
+                "C*depth*D_ctx too large: the context K/V weights [2C*depth][D_ctx] reach 2^31 bytes");
   if (!w) return fail(ST_ERR_INVALID, "weights are NULL");
   if (!w->layers) return fail(ST_ERR_INVALID, "weights.layers is NULL");
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };
@@ -279,8 +290,8 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->bytes_planned = 0;
   b->bytes_cap = 0;
   if (const char* cap = std::getenv("ST_MAX_DEVICE_BYTES")) b->bytes_cap = std::strtoull(cap, nullptr, 10);
-  b->last_stream = static_cast<hipStream_t>(stream);
   b->timing_mask = 0;
+  b->range_flag = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Creator cr{b, s};
@@ -293,6 +304,8 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   if (b->bf16) {
     cr.overflow = static_cast<int*>(cr.alloc(sizeof(int), "overflow flag"));
     if (cr.overflow) cr.dev(hipMemsetAsync(cr.overflow, 0, sizeof(int), s), "overflow flag");
+    b->range_flag = static_cast<int*>(cr.alloc(sizeof(int), "range flag"));
+    if (b->range_flag) cr.dev(hipMemsetAsync(b->range_flag, 0, sizeof(int), s), "range flag");
   }
   b->w_in = cr.mat(w->proj_in_w, C, C, "proj_in_w");
   cr.to_f16(b->w_in, CC, "proj_in_w to fp16");
@@ -560,6 +573,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     p.epi.out_f32 = nullptr;
     p.epi.out_act = b->hcopy;
     p.epi.row_stats = b->hstats;
+    p.epi.range_flag = b->range_flag;
   };
   // K slices of a residual product (bf16 path; set at create)
   auto split_k = [&](GemmParams& p, int slices) {
@@ -588,7 +602,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
          }), "GroupNorm statistics");
   ST_TRY(run(b, ST_K_PROJ_IN, s, [&] {
            hipError_t e = gn_apply_tokens(x, bf, b->gn_part, b->gn_max_split, b->gn_w, b->gn_b,
-                                          b->u, act, B, C, N, s);
+                                          b->u, act, B, C, N, b->range_flag, s);
            if (e != hipSuccess) return e;
            GemmParams p = gemm(b->u, C, b->w_in, C, T, C, C, EPI_STORE_F32);
            p.epi.bias = b->b_in; p.epi.out_f32 = b->h; p.epi.ldo = C;
@@ -706,6 +720,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
                GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_GEGLU);
                normed(p, L, 2);
                p.epi.bias = L.b1; p.epi.out_act = b->f; p.epi.F = F;
+               p.epi.range_flag = b->range_flag;
                return gemm_mfma(p, ACT_F16, s);
              }
              GemmParams p = gemm(b->u, C, L.w1, C, T, 2 * F, C, EPI_STORE_F32);
@@ -784,9 +799,7 @@ ST_API st_status st_block_forward(st_block* b, const void* x, const void* ctx,
   if (st != ST_OK) return st;
   DeviceGuard g(b->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "select device");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  b->last_stream = s;
-  return forward_impl(b, x, ctx, y, -1, nullptr, s);
+  return forward_impl(b, x, ctx, y, -1, nullptr, static_cast<hipStream_t>(stream));
 }
 
 ST_API st_status st_block_forward_stage(st_block* b, const void* x,
@@ -800,23 +813,112 @@ ST_API st_status st_block_forward_stage(st_block* b, const void* x,
   if (stage < 0 || stage > 3 * b->depth) return fail(ST_ERR_INVALID, "stage out of range");
   DeviceGuard g(b->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "select device");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  b->last_stream = s;
-  return forward_impl(b, x, ctx, nullptr, stage, h_out, s);
+  return forward_impl(b, x, ctx, nullptr, stage, h_out, static_cast<hipStream_t>(stream));
 }
 
 ST_API void st_block_destroy(st_block* b) {
   if (!b) return;
   DeviceGuard g(b->device);
-  (void)hipStreamSynchronize(b->last_stream);
+  // Forwards may have been enqueued on any number of streams (some perhaps
+  // destroyed by now): waiting for the whole device covers every one.
+  (void)hipDeviceSynchronize();
+  (void)hipGetLastError();
   free_all(b);
   delete b;
+}
+
+ST_API st_status st_block_check_range(st_block* b, void* stream) {
+  g_err.clear();
+  if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
+  if (!b->range_flag) return ST_OK;  // fp32 storage keeps no fp16 intermediates
+  DeviceGuard g(b->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "select device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, b->range_flag, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "read the range flag");
+  if (!flag) return ST_OK;
+  e = hipMemsetAsync(b->range_flag, 0, sizeof(int), s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "clear the range flag");
+  return fail(ST_ERR_RANGE,
+              "an fp16 intermediate (residual stream, GEGLU output or normalised input) "
+              "left the fp16 range (|value| >= 65520 or NaN): outputs of the forwards since "
+              "the last check are not valid");
 }
 
 ST_API st_status st_block_set_timing(st_block* b, unsigned kind_mask) {
   g_err.clear();
   if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
   b->timing_mask = kind_mask & ((1u << ST_K_COUNT) - 1u);
+  return ST_OK;
+}
+
+ST_API st_status st_block_read_timing_launches(st_block* b, int* kinds, double* ms,
+                                              long long capacity, long long* count) {
+  g_err.clear();
+  if (!b || !count || (capacity > 0 && (!kinds || !ms)))
+    return fail(ST_ERR_INVALID, "handle, count, kinds or ms is NULL");
+  st_status st = ST_OK;
+  long long n = 0;
+  for (auto& t : b->pending) {
+    float v = 0.f;
+    hipError_t e = hipEventElapsedTime(&v, t.e0, t.e1);
+    if (e != hipSuccess && st == ST_OK) st = hip_fail(e, "hipEventElapsedTime (stream not synchronised?)");
+    if (n < capacity) {
+      kinds[n] = t.kind;
+      ms[n] = v;
+    }
+    ++n;
+    b->spare_events.push_back(t.e0);
+    b->spare_events.push_back(t.e1);
+  }
+  b->pending.clear();
+  *count = n;
+  return st;
+}
+
+ST_API st_status st_measure_mfma_bf16(int iters, void* stream, double* tflops,
+                                      double* sclk_mhz) {
+  g_err.clear();
+  if (!tflops || !sclk_mhz || iters < 1) return fail(ST_ERR_INVALID, "bad arguments");
+  int dev = 0, cus = 0, wall_khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return hip_fail(e, "device attributes");
+  const int grid = mfma_probe_grid(cus);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* out = nullptr;
+  long long* clocks = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  std::vector<long long> host(2 * static_cast<size_t>(grid));
+  float ms = 0.f;
+  e = hipMalloc(&out, sizeof(float) * 256 * grid);
+  if (e == hipSuccess) e = hipMalloc(&clocks, sizeof(long long) * 2 * grid);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = mfma_probe(grid, iters, out, clocks, s);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  if (e == hipSuccess) e = mfma_probe(grid, iters, out, clocks, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e == hipSuccess)
+    e = hipMemcpy(host.data(), clocks, sizeof(long long) * 2 * grid, hipMemcpyDeviceToHost);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (out) (void)hipFree(out);
+  if (clocks) (void)hipFree(clocks);
+  if (e != hipSuccess) return hip_fail(e, "MFMA probe");
+  double cyc = 0.0, ticks = 0.0;
+  for (int i = 0; i < grid; ++i) {
+    cyc += static_cast<double>(host[2 * i]);
+    ticks += static_cast<double>(host[2 * i + 1]);
+  }
+  *tflops = static_cast<double>(mfma_probe_flops(grid, iters)) / (ms * 1e-3) / 1e12;
+  *sclk_mhz = ticks > 0.0 ? cyc / ticks * (wall_khz / 1000.0) : 0.0;
   return ST_OK;
 }
 

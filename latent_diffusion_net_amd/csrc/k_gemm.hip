@@ -289,6 +289,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
     }
     f16_t* h16 = static_cast<f16_t*>(p.epi.out_act);
+    bool bad = false;  // a stored value is not finite
     // all residual rows are loaded before the first store (the compiler
     // cannot prove a store to h disjoint from the next row's load)
     uint4 hin[8];
@@ -326,6 +327,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       const uint4 w = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]), pack2h(v[4], v[5]),
                                  pack2h(v[6], v[7]));
       *reinterpret_cast<uint4*>(h16 + static_cast<long long>(row) * p.epi.ldo + C0 + lc) = w;
+      bad |= f16x8_nonfinite(w);
       if (p.epi.row_stats) {
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -345,6 +347,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
           p.epi.row_stats[static_cast<long long>(row) * (p.epi.ldo >> 6) + (C0 >> 6)] = make_float2(sum, m2);
       }
     }
+    if (bad && p.epi.range_flag) *p.epi.range_flag = 1;
   } else if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID_F32) {
     constexpr bool kRes = EPI == EPI_RESID_F32;
     // lane -> 4 consecutive columns of one row; 4 rows per pass
@@ -409,6 +412,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
       lgv = *reinterpret_cast<const float4*>(ln_cols + lc);
       lgg = *reinterpret_cast<const float4*>(ln_cols + 32 + lc);
     }
+    bool bad = false;  // a stored value is not finite
 #pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int lr = it * 8 + (lane >> 3);
@@ -425,7 +429,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
           pack2h((v.x + bv[0]) * gelu_as(g.x + bg[0]), (v.y + bv[1]) * gelu_as(g.y + bg[1])),
           pack2h((v.z + bv[2]) * gelu_as(g.z + bg[2]), (v.w + bv[3]) * gelu_as(g.w + bg[3])));
       *reinterpret_cast<uint2*>(out + static_cast<long long>(row) * F + fc0 + lc) = pk;
+      bad |= f16_pair_nonfinite(pk.x) | f16_pair_nonfinite(pk.y);
     }
+    if (bad && p.epi.range_flag) *p.epi.range_flag = 1;
   } else if constexpr (EPI == EPI_HEADS) {
     // The 64 columns are one head of one split (C0 and C are multiples of
     // 64).
@@ -954,6 +960,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_h16_kernel(GemmParams p) {
   const uint4 o = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]), pack2h(v[4], v[5]),
                              pack2h(v[6], v[7]));
   *reinterpret_cast<uint4*>(h16) = o;
+  if (p.epi.range_flag && f16x8_nonfinite(o)) *p.epi.range_flag = 1;
   if (p.epi.row_stats) {
     const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll

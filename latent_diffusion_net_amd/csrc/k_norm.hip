@@ -107,17 +107,22 @@ hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,
   return hipGetLastError();
 }
 
+// Eight values stored; returns true when a stored value is not finite
+// (fp16 only: fp32 keeps the range of its inputs).
 template <typename T>
-__device__ __forceinline__ void store8(T* p, const float v[8]);
+__device__ __forceinline__ bool store8(T* p, const float v[8]);
 template <>
-__device__ __forceinline__ void store8<f16_t>(f16_t* p, const float v[8]) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]),
-                                            pack2h(v[4], v[5]), pack2h(v[6], v[7]));
+__device__ __forceinline__ bool store8<f16_t>(f16_t* p, const float v[8]) {
+  const uint4 w = make_uint4(pack2h(v[0], v[1]), pack2h(v[2], v[3]), pack2h(v[4], v[5]),
+                             pack2h(v[6], v[7]));
+  *reinterpret_cast<uint4*>(p) = w;
+  return f16x8_nonfinite(w);
 }
 template <>
-__device__ __forceinline__ void store8<float>(float* p, const float v[8]) {
+__device__ __forceinline__ bool store8<float>(float* p, const float v[8]) {
   reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  return false;
 }
 
 // Apply GroupNorm and transpose NCHW -> tokens [B*N][C] through LDS.  A
@@ -131,7 +136,7 @@ template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
     const TI* __restrict__ x, const float2* __restrict__ partial, int split,
     const float* __restrict__ gamma, const float* __restrict__ beta,
-    TO* __restrict__ out, int C, int N) {
+    TO* __restrict__ out, int C, int N, int* __restrict__ range_flag) {
   __shared__ float2 coef[64];
   __shared__ float tile[64][64 + 4];  // [channel][token]
   const int n0 = blockIdx.x * 64;
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
     for (int j = 0; j < 8; ++j) tile[cl][nl + j] = v[j] * k.x + k.y;
   }
   __syncthreads();
+  bool bad = false;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int nl = pass * 32 + (tid >> 3);
@@ -186,24 +192,25 @@ __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = tile[cl + j][nl];
-    store8<TO>(out + (static_cast<long long>(b) * N + n) * C + c0 + cl, v);
+    bad |= store8<TO>(out + (static_cast<long long>(b) * N + n) * C + c0 + cl, v);
   }
+  if (bad && range_flag) *range_flag = 1;
 }
 
 hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
                            int max_split, const float* gamma, const float* beta,
                            void* out, int out_type, int B, int C, int N,
-                           hipStream_t s) {
+                           int* range_flag, hipStream_t s) {
   const int split = gn_split(C, N, max_split);
   dim3 grid((N + 63) / 64, C / 64, B);
   if (bf16 && out_type == ACT_F16)
     gn_apply_tokens_kernel<bf16_t, f16_t><<<grid, 256, 0, s>>>(
         static_cast<const bf16_t*>(x), partial, split, gamma, beta,
-        static_cast<f16_t*>(out), C, N);
+        static_cast<f16_t*>(out), C, N, range_flag);
   else if (!bf16 && out_type == ACT_F32)
     gn_apply_tokens_kernel<float, float><<<grid, 256, 0, s>>>(
         static_cast<const float*>(x), partial, split, gamma, beta,
-        static_cast<float*>(out), C, N);
+        static_cast<float*>(out), C, N, nullptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -80,6 +80,10 @@ struct EpiParams {
   int ln_blocks;
   float ln_eps;
   CrossAttn ca;  // EPI_CROSS_ATTN (output: out_act, row stride ldo)
+  // fp16 outputs (EPI_STORE_H16, EPI_RESID_H16, EPI_GEGLU and their split-K
+  // pass): set to 1 when a stored value is not finite (an fp32 value at or
+  // beyond 65520 in magnitude rounds to infinity); may be NULL
+  int* range_flag;
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T, then the epilogue.
@@ -151,10 +155,12 @@ void attention_bf16_plan(int B, int heads, int Nq, int Nk, int cus, int& n_full,
 hipError_t gn_stats(const void* x, bool bf16, int B, int C, int N,
                     float2* partial, int max_split, hipStream_t s);
 int gn_split(int C, int N, int max_split);
+// With an fp16 output, *range_flag (may be NULL) is set to 1 when a stored
+// value is not finite.
 hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
                            int max_split, const float* gamma, const float* beta,
                            void* out, int out_type, int B, int C, int N,
-                           hipStream_t s);
+                           int* range_flag, hipStream_t s);
 // u: [T][C] of type `out_type` (ACT_F32, ACT_BF16 or ACT_F16).
 hipError_t layernorm(const float* h, const float* gamma, const float* beta,
                      void* u, int out_type, int T, int C, hipStream_t s);
@@ -180,5 +186,14 @@ hipError_t weight_fold_layernorm(void* w, int rows, int C, const float* gamma,
 // dst row r = src row map[r], rows of `row_bytes` bytes (multiple of 16).
 hipError_t gather_rows(const void* src, void* dst, const int* map, int rows,
                        long long row_bytes, hipStream_t s);
+
+// Matrix-pipe probe (k_probe.hip): `grid` workgroups of four wavefronts,
+// each running four independent bf16 32x32x16 MFMA chains for `iters`
+// rounds.  out: grid * 256 floats (the sums, kept live); clocks: 2 * grid
+// values, per workgroup the shader cycles and the real-time ticks of the
+// loop.
+int mfma_probe_grid(int cus);
+long long mfma_probe_flops(int grid, int iters);
+hipError_t mfma_probe(int grid, int iters, float* out, long long* clocks, hipStream_t s);
 
 }  // namespace stb

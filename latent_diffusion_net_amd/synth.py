@@ -110,12 +110,16 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 
 def make_inputs(cfg: BlockConfig, seed: int, *, weight_std: float = 0.02,
                 bias_std: float = 0.0, norm_std: float = 0.0,
-                x_std: float = 1.0) -> Dict:
+                x_std: float = 1.0, qk_std: Optional[float] = None) -> Dict:
     """Draw x, ctx and every parameter of the block.
 
     ``bias_std`` > 0 draws every bias ~ N(0, bias_std^2); ``norm_std`` > 0 draws
-    gammas ~ N(1, norm_std^2) and betas ~ N(0, norm_std^2).  Both are stress
-    options; the headline workloads keep them at 0.
+    gammas ~ N(1, norm_std^2) and betas ~ N(0, norm_std^2).  ``qk_std`` scales
+    the query and key weights of both attentions (q1, k1, q2, k2) instead of
+    ``weight_std`` -- the same standard-normal draws, so only the sharpness
+    of the softmax changes: with unit-variance normalised tokens the logits
+    have standard deviation about qk_std^2 * C.  All three are stress
+    options; the headline workloads keep the defaults.
     """
     rng = np.random.default_rng(seed)
     f32 = np.float32
@@ -130,9 +134,11 @@ def make_inputs(cfg: BlockConfig, seed: int, *, weight_std: float = 0.02,
     shapes = {"q1_w": (C, C), "k1_w": (C, C), "v1_w": (C, C), "o1_w": (C, C),
               "q2_w": (C, C), "k2_w": (C, D), "v2_w": (C, D), "o2_w": (C, C),
               "ff1_w": (2 * F, C), "ff2_w": (C, F)}
+    qk = ("q1_w", "k1_w", "q2_w", "k2_w")
     layers = []
     for _ in range(cfg.depth):
-        layers.append({k: normal(shapes[k], weight_std) for k in LAYER_WEIGHTS})
+        layers.append({k: normal(shapes[k], qk_std if (qk_std is not None and k in qk) else weight_std)
+                       for k in LAYER_WEIGHTS})
     proj_out_w = normal((C, C), weight_std)
 
     rng2 = np.random.default_rng(seed + 7919)

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "st_block.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(st_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(st_[a-z0-9_]+)\s*\(", src)))
 
 
 def _lib():
@@ -146,16 +146,50 @@ def _load_fresh(path):
 
 
 def test_create_rejects_shapes_beyond_32bit_offsets():
-    """The kernels index activations with 32-bit element offsets; the
-    largest buffer, the GEGLU output [B*H*W][4C], must stay below 2^31
-    elements.  Checked before any device call."""
+    """The GEMMs address each operand with 32-bit byte offsets; create
+    refuses every shape whose operands reach 2^31 bytes, before any device
+    call, so that a forward on a created handle never fails half-way."""
     lib = _lib()
     bw, _keep = _fake_weights()
     # 1 x 1024 x 1024 tokens x 4*1280 = 5.4e9 elements
     st, h = _create(lib, B=1, C=1280, H=1024, W=1024, heads=20, w=bw)
     assert st == binding.ST_ERR_UNSUPPORTED
     assert h.value is None
-    assert "2^31" in binding.last_error()
-    # just past the limit: 2^31 elements exactly
+    assert "2^30" in binding.last_error()
+    # 2^31 elements exactly
     st, h = _create(lib, B=2, C=64, H=2048, W=2048, heads=1, w=bw)
     assert st == binding.ST_ERR_UNSUPPORTED and h.value is None
+    # just above 2^30 elements of the GEGLU output (2^31 bytes of FF2's A
+    # operand): B=4, C=1280, 256 x 256 -> T*4C = 1.34e9
+    st, h = _create(lib, B=4, C=1280, H=256, W=256, heads=20, w=bw)
+    assert st == binding.ST_ERR_UNSUPPORTED and h.value is None
+    assert "FF2" in binding.last_error()
+    # T*4C = 2^30 exactly: 2^31 bytes, refused; one token fewer per sample
+    # reaches the device (no GPU here: ST_ERR_DEVICE, or a handle with one)
+    st, h = _create(lib, B=1, C=64, H=2048, W=2048, heads=1, w=bw)
+    assert st == binding.ST_ERR_UNSUPPORTED and h.value is None
+
+
+@pytest.mark.parametrize("kw,what", [
+    # FF1 weights [8C][C] in 16-bit: 16*C^2 bytes >= 2^31 from C = 11648
+    (dict(C=11648, heads=182, H=1, W=1), "FF1"),
+    # context K/V weights [2C*depth][D] in 16-bit: 4*C*depth*D >= 2^31
+    (dict(C=1280, heads=20, depth=10, D=41984, H=1, W=1), "context K/V"),
+])
+def test_create_rejects_large_weight_operands(kw, what):
+    lib = _lib()
+    bw, _keep = _fake_weights(depth=kw.get("depth", 1))
+    st, h = _create(lib, w=bw, **kw)
+    assert st == binding.ST_ERR_UNSUPPORTED and h.value is None
+    assert what in binding.last_error()
+
+
+def test_null_handle_new_entry_points():
+    lib = _lib()
+    assert lib.st_block_check_range(None, None) == binding.ST_ERR_INVALID
+    n = ctypes.c_longlong()
+    assert lib.st_block_read_timing_launches(None, None, None, 0, ctypes.byref(n)) \
+        == binding.ST_ERR_INVALID
+    d = ctypes.c_double()
+    assert lib.st_measure_mfma_bf16(0, None, ctypes.byref(d), ctypes.byref(d)) \
+        == binding.ST_ERR_INVALID

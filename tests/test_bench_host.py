@@ -87,20 +87,23 @@ def test_traffic_figure_is_tied_to_the_kernel_source(bench, tmp_path, monkeypatc
 
 
 def test_row_work_adds_up_to_block_flops(bench):
-    """The per-kernel work of the roofline rows, counted per forward, plus the
-    cross-attention contractions (charged to the HBM-bound row by bytes)
-    is every FLOP of the block."""
+    """The per-kernel flops of the MFMA-bound rows, counted per forward, plus
+    the context K/V product (rated by its bytes) and, where the
+    cross-attention has a launch of its own, its contractions, are every
+    FLOP of the block."""
     from latent_diffusion_net_amd import synth
     for cfg in synth.CONFIGS:
         work = bench.row_work(cfg)
-        per_forward = {"proj_in": 1, "proj_out": 1, "ctx_kv": 1}
+        per_forward = {"proj_in": 1, "proj_out": 1}
         for k in ("qkv", "self_attn", "cross_q", "ff1_geglu", "ff2"):
             per_forward[k] = cfg.depth
         per_forward["attn_out"] = 2 * cfg.depth
         total = sum(work[k][2] * n for k, n in per_forward.items())
         assert all(work[k][1] == "mfma" for k in per_forward)
-        cross = cfg.depth * 4.0 * cfg.B * cfg.N * 77 * cfg.C
-        assert abs(total + cross - bench.block_flops(cfg)) <= 1e-9 * bench.block_flops(cfg)
+        assert work["ctx_kv"][1] == "hbm"
+        ctx = 2.0 * cfg.B * 77 * 2 * cfg.C * cfg.depth * cfg.D_ctx
+        cross = 0.0 if bench.fused_cross(cfg) else cfg.depth * 4.0 * cfg.B * cfg.N * 77 * cfg.C
+        assert abs(total + ctx + cross - bench.block_flops(cfg)) <= 1e-9 * bench.block_flops(cfg)
 
 
 def test_row_rates_units(bench):
@@ -120,3 +123,26 @@ def test_row_rates_units(bench):
     r2 = bench.row_rates(cfg, {"self_attn": {"ms": 0.2, "launches": 2}}, 5000.0)
     assert r2["A3/A7/A12 LayerNorm"] == {"fused": bench.LAYERNORM_FOLDED}
     assert r2["A10 cross-attention"] == {"fused": bench.CROSS_ATTN_FUSED}
+
+
+def test_row_work_rates_context_kv_on_hbm_and_counts_fused_cross_attention(bench):
+    from latent_diffusion_net_amd import synth
+    cfg = synth.CONFIGS[3]  # SDXL Down1: H*W % 64 == 0, cross-attention fused into cross Q
+    T, C, B, N, D, depth = cfg.T, cfg.C, cfg.B, cfg.N, cfg.D_ctx, cfg.depth
+    w = bench.row_work(cfg)
+    name, bound, work = w["ctx_kv"]
+    assert bound == "hbm"
+    # weights of every layer, the context, and K/V written: 2 bytes each
+    assert work == 2.0 * (2 * C * depth * D + B * 77 * D + 2 * B * 77 * C * depth)
+    # the GEMM's intensity is below the ridge, so HBM is the right roofline
+    flops = 2.0 * B * 77 * 2 * C * depth * D
+    assert flops / work < 2.5e15 / 8e12
+    name, bound, work = w["cross_q"]
+    assert bound == "mfma"
+    assert work == 2.0 * T * C * C + 4.0 * B * N * 77 * C
+    odd = synth.BlockConfig("odd", 1, 64, 5, 5, 1, 64, 1, "bf16")  # separate cross-attention launch
+    assert bench.row_work(odd)["cross_q"][2] == 2.0 * odd.T * 64 * 64
+
+
+def test_cpu_model_is_reported(bench):
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

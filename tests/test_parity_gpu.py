@@ -294,3 +294,104 @@ def test_self_attention_split_over_keys(cus, spec, monkeypatch):
     y = y1.float().cpu().numpy().astype(np.float64)
     blk.close()
     check(cfg, inp, y, yo)
+
+
+@pytest.mark.parametrize("spec", __import__("sa_stage").SHAPES, ids=lambda s: s["name"])
+def test_self_attention_sharp(spec, monkeypatch):
+    """The self-attention path the workloads time, with a softmax far from
+    flat (logit std about 3): the 128-query kernel at the full SDXL Down1
+    shape (whole tiles, key-split pieces and their merge), with ragged
+    queries and keys, and the forced key-split plans.  The sublayer's update
+    (stage 1 minus stage 0 of the GPU's own stream) against the oracle's
+    l0_sa - h0, element by element; bounds and the mutations they reject in
+    tests/sa_stage.py and tests/test_sa_stage_pins.py."""
+    import torch
+    import sa_stage as sa
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    if spec["cus"] is not None:
+        monkeypatch.setenv("ST_ATTN_CUS", str(spec["cus"]))
+    cfg, inp = sa.inputs(spec)
+    _say(f"[gpu] sharp self-attention {cfg.name}: B={cfg.B} C={cfg.C} N={cfg.N} "
+         f"planned CUs={spec['cus']}")
+    p = params_to_device(inp["params"], "bf16")
+    x = array_to_device(inp["x"], "bf16")
+    ctx = array_to_device(inp["ctx"], "bf16")
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+    del p
+    g0 = blk.forward_stage(x, ctx, 0)
+    g1 = blk.forward_stage(x, ctx, 1)
+    g1b = blk.forward_stage(x, ctx, 1)
+    blk.check_range()
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g1b)  # pieces merged in a fixed order
+    d_gpu = (g1 - g0).cpu().numpy().astype(np.float64)
+    blk.close()
+    del g0, g1, g1b
+    h0, h1 = sa.oracle_stage1(inp, cfg.heads)
+    d_ref = (h1 - h0).reshape(d_gpu.shape)
+    rel, mx = sa.update_errors(d_gpu, d_ref)
+    _say(f"    update rel_l2={rel:.3e} max_abs/max|update|={mx:.3e}")
+    assert np.isfinite(d_gpu).all()
+    assert rel <= sa.UPDATE_REL_L2, rel
+    assert mx <= sa.UPDATE_MAX_ABS_REL, mx
+
+
+def _offset_stream_inputs(cfg, seed, offset):
+    """Headline draws, with proj_in's bias = offset on every channel, so each
+    row of the residual stream h has mean ~offset and std ~0.02 sqrt(C);
+    proj_out's bias cancels the offset's image in y (b_out = -offset *
+    row sums of W_out, rounded to bf16: the same values on both sides), so y
+    keeps its usual scale."""
+    inp = synth.make_inputs(cfg, seed)
+    p = inp["params"]
+    C = cfg.C
+    p["proj_in_b"] = synth.round_bf16(np.full(C, offset, np.float32))
+    rs = np.asarray(p["proj_out_w"], np.float64).sum(axis=1)
+    p["proj_out_b"] = synth.round_bf16((-float(p["proj_in_b"][0]) * rs).astype(np.float32))
+    return inp
+
+
+def test_fp16_stream_large_row_mean():
+    """Rows of h whose mean is ~30 standard deviations away from zero (h0 =
+    15 + N(0, 0.51^2) at C = 640): the fp16 stream rounds them with an
+    absolute error ~30x larger relative to their spread than usual, and the
+    folded LayerNorm subtracts the mean after the product.  The output still
+    meets the bf16 gate and no range error is raised."""
+    cfg = synth.BlockConfig("offset15_c640_32x32_d2", 1, 640, 32, 32, 10, 256, 2, "bf16")
+    inp = _offset_stream_inputs(cfg, 13, 15.0)
+    _, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
+                                intermediates=True)
+    h0 = inter["h0"]
+    ratio = np.abs(h0.mean(axis=-1)) / h0.std(axis=-1)
+    _say(f"    |mean|/std of the rows of h0: median {np.median(ratio):.1f}")
+    assert np.median(ratio) > 25
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    y, _ = run_gpu(cfg, inp)
+    check(cfg, inp, y, yo)
+
+
+def test_fp16_stream_overflow_is_reported():
+    """A proj_in bias of 70144 puts every value of h beyond the fp16 range:
+    st_block_check_range reports ST_ERR_RANGE (then the flag is clear);
+    the same block with an in-range bias reports nothing."""
+    import torch
+    from latent_diffusion_net_amd import STBlock, STError, array_to_device, params_to_device
+    from latent_diffusion_net_amd.binding import ST_ERR_RANGE
+    cfg = synth.BlockConfig("overflow_c128", 1, 128, 8, 8, 2, 128, 1, "bf16")
+    _say("[gpu] fp16 range flag")
+    for offset, expect in ((70144.0, True), (15.0, False)):
+        inp = _offset_stream_inputs(cfg, 17, offset)
+        p = params_to_device(inp["params"], "bf16")
+        x = array_to_device(inp["x"], "bf16")
+        ctx = array_to_device(inp["ctx"], "bf16")
+        blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, "bf16", p)
+        y = blk.forward(x, ctx)
+        if expect:
+            with pytest.raises(STError) as e:
+                blk.check_range()
+            assert e.value.status == ST_ERR_RANGE
+        blk.check_range()  # clear (or never set)
+        torch.cuda.synchronize()
+        if not expect:
+            assert torch.isfinite(y.float()).all()
+        blk.close()
