@@ -109,8 +109,9 @@ def layer_norm(h, gamma, beta, eps: float = LN_EPS):
 
 
 def attention(q, k, v, heads: int, row_block: int = 2048,
-              return_probs: bool = False, rows: Optional[np.ndarray] = None):
-    """Multi-head scaled dot-product attention, no mask.
+              return_probs: bool = False, rows: Optional[np.ndarray] = None,
+              key_mask: Optional[np.ndarray] = None):
+    """Multi-head scaled dot-product attention.
 
     q: [B, Nq, C], k and v: [B, Nk, C], C = heads * 64.  Head ``hd`` takes the
     contiguous channel slice [64*hd, 64*hd + 64) of each projection (the
@@ -123,6 +124,13 @@ def attention(q, k, v, heads: int, row_block: int = 2048,
     larger than row_block x Nk is ever held; this changes no arithmetic.
     ``rows`` restricts the computation to the listed query rows (per batch).
     ``return_probs`` also returns P as [B, heads, Nq, Nk] (small inputs only).
+
+    ``key_mask`` ([B, Nk], nonzero = attend) excludes keys from the softmax:
+    the anatomy article's §5.5 ("Cross-Attention mask") passes the
+    tokenizer's attention_mask, 0 marking a padding token, so that padding
+    positions take no part.  Reading taken: a masked key gets probability 0
+    (the softmax runs over the unmasked keys only); a row of sample b whose
+    every key is masked has no keys to average and outputs 0.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Nq, C = q.shape
@@ -135,12 +143,20 @@ def attention(q, k, v, heads: int, row_block: int = 2048,
     out = np.empty((B, nq, C), dtype=np.float64)
     probs = np.empty((B, heads, nq, k.shape[1])) if return_probs else None
     for b in range(B):
+        keep = None if key_mask is None else np.asarray(key_mask)[b] != 0
         for hd in range(heads):
             sl = slice(hd * d, (hd + 1) * d)
             kh, vh = k[b, :, sl], v[b, :, sl]
             for r0 in range(0, nq, row_block):
                 qh = qi[b, r0:r0 + row_block, sl]
+                if keep is not None and not keep.any():
+                    out[b, r0:r0 + row_block, sl] = 0.0
+                    if return_probs:
+                        probs[b, hd, r0:r0 + row_block] = 0.0
+                    continue
                 s = (qh @ kh.T) * scale
+                if keep is not None:
+                    s = np.where(keep[None, :], s, -np.inf)
                 s = s - s.max(axis=1, keepdims=True)
                 e = np.exp(s)
                 p = e / e.sum(axis=1, keepdims=True)
@@ -178,13 +194,16 @@ def self_attention_sublayer(h, lw, heads):
     return h + linear(o, lw["o1_w"], lw.get("o1_b"))
 
 
-def cross_attention_sublayer(h, ctx, lw, heads):
-    """h + Attn(Q = LN2(h) Wq, K = ctx Wk, V = ctx Wv); ctx is not normalised."""
+def cross_attention_sublayer(h, ctx, lw, heads, ctx_mask=None):
+    """h + Attn(Q = LN2(h) Wq, K = ctx Wk, V = ctx Wv); ctx is not normalised.
+
+    ``ctx_mask`` ([B, 77], nonzero = a real token): the context's key
+    padding mask (see ``attention``)."""
     u = layer_norm(h, lw["ln2_w"], lw["ln2_b"])
     q = linear(u, lw["q2_w"], lw.get("q2_b"))
     k = linear(ctx, lw["k2_w"], lw.get("k2_b"))
     v = linear(ctx, lw["v2_w"], lw.get("v2_b"))
-    o = attention(q, k, v, heads)
+    o = attention(q, k, v, heads) if ctx_mask is None else attention(q, k, v, heads, key_mask=ctx_mask)
     return h + linear(o, lw["o2_w"], lw.get("o2_b"))
 
 
@@ -197,7 +216,7 @@ def feed_forward_sublayer(h, lw):
 
 
 def block_forward(x, ctx, params: Dict, heads: int,
-                  intermediates: bool = False):
+                  intermediates: bool = False, ctx_mask=None):
     """The whole Spatial-Transformer block, [B, C, H, W] -> [B, C, H, W].
 
     GroupNorm -> flatten to tokens -> proj_in -> depth x (self-attention,
@@ -206,7 +225,8 @@ def block_forward(x, ctx, params: Dict, heads: int,
 
     With ``intermediates`` the function also returns a dict holding the
     fp64 residual stream after proj_in ("h0") and after each sublayer
-    ("l{i}_sa", "l{i}_ca", "l{i}_ff").
+    ("l{i}_sa", "l{i}_ca", "l{i}_ff").  ``ctx_mask`` ([B, 77]) masks padding
+    tokens of the context out of every cross-attention.
     """
     x = _f64(x)
     ctx = _f64(ctx)
@@ -217,7 +237,7 @@ def block_forward(x, ctx, params: Dict, heads: int,
     for i, lw in enumerate(params["layers"]):
         h = self_attention_sublayer(h, lw, heads)
         inter[f"l{i}_sa"] = h
-        h = cross_attention_sublayer(h, ctx, lw, heads)
+        h = cross_attention_sublayer(h, ctx, lw, heads, ctx_mask)
         inter[f"l{i}_ca"] = h
         h = feed_forward_sublayer(h, lw)
         inter[f"l{i}_ff"] = h

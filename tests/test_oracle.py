@@ -2,8 +2,10 @@
 import pytest
 
 import oracle_pins
+import oracle_pins_unet
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle_pins_unet.ALL_PINS,
+                         ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin()
