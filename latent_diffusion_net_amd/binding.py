@@ -32,11 +32,12 @@ LAYER_FIELDS = ("ln1_w", "ln1_b", "q1_w", "k1_w", "v1_w", "q1_b", "k1_b",
 BLOCK_FIELDS = ("gn_w", "gn_b", "proj_in_w", "proj_in_b", "proj_out_w",
                 "proj_out_b")
 
-# Every function include/st_block.h declares.
+# Every function include/st_block.h and include/st_ops.h declare.
 EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_stage",
            "st_block_destroy", "st_block_check_range", "st_last_error",
            "st_block_set_timing", "st_block_read_timing",
-           "st_block_read_timing_launches", "st_measure_mfma_bf16")
+           "st_block_read_timing_launches", "st_measure_mfma_bf16",
+           "st_group_norm_workspace_bytes", "st_group_norm", "st_guided_ddpm_step")
 
 
 class LayerWeights(ctypes.Structure):
@@ -103,6 +104,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_block_read_timing_launches.restype = i
     lib.st_measure_mfma_bf16.argtypes = [i, vp, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
     lib.st_measure_mfma_bf16.restype = i
+    f32, sz = ctypes.c_float, ctypes.c_size_t
+    lib.st_group_norm_workspace_bytes.argtypes = [i]
+    lib.st_group_norm_workspace_bytes.restype = sz
+    lib.st_group_norm.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp, sz, vp]
+    lib.st_group_norm.restype = i
+    lib.st_guided_ddpm_step.argtypes = [vp, i, vp, vp, vp, ll, f32, i, i, dbl, dbl, vp]
+    lib.st_guided_ddpm_step.restype = i
     _lib = lib
     return lib
 
@@ -221,6 +229,51 @@ class STBlock:
             self.close()
         except Exception:
             pass
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ST_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ST_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def group_norm(x, gamma=None, beta=None, eps: float = 1e-5, silu: bool = False,
+               y=None, workspace=None, stream=None):
+    """y = [SiLU](GroupNorm_32(x)) on an NCHW device tensor (st_group_norm).
+    ``workspace``: a device tensor of at least st_group_norm_workspace_bytes(B)
+    bytes (allocated here when None)."""
+    import torch
+    lib = load_library()
+    B, C, H, W = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    need = lib.st_group_norm_workspace_bytes(B)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.st_group_norm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), B, C, H, W, eps,
+                             1 if silu else 0, _dtype_code(x), _ptr(workspace), nbytes,
+                             _stream_handle(stream)))
+    return y
+
+
+def guided_ddpm_step(eps_pair, x_t, t: int, guidance_scale: float, noise=None, x_prev=None,
+                     T: int = 1000, beta_start: float = 1e-4, beta_end: float = 0.02,
+                     stream=None):
+    """x_{t-1} from x_t (fp32) and the pair's noise predictions [2, ...]
+    (unconditional first), with guidance and the linear DDPM schedule."""
+    import torch
+    lib = load_library()
+    if x_prev is None:
+        x_prev = torch.empty_like(x_t)
+    n = x_t.numel()
+    _check(lib.st_guided_ddpm_step(_ptr(eps_pair), _dtype_code(eps_pair), _ptr(x_t), _ptr(noise),
+                                   _ptr(x_prev), n, guidance_scale, t, T, beta_start, beta_end,
+                                   _stream_handle(stream)))
+    return x_prev
 
 
 def measure_mfma_bf16(iters: int = 16384, stream=None):

@@ -222,6 +222,12 @@ struct Creator {
 
 }  // namespace
 
+// Error text of this host thread, shared with the other ABI sources.
+st_status st_set_error(st_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
 // ======================================================================= ABI
 
 ST_API const char* st_last_error(void) { return g_err.c_str(); }

@@ -216,6 +216,132 @@ hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
   return hipGetLastError();
 }
 
+// GroupNorm apply on NCHW -> NCHW (the standalone GroupNorm op), optionally
+// followed by SiLU.  A workgroup takes 2048 elements of one (sample,
+// channel) plane: wavefront 0 first combines the group's partial sums in
+// fp64 into the channel's (scale, offset), then every thread moves eight
+// consecutive elements (16-byte accesses when the plane allows).
+template <typename T>
+__global__ __launch_bounds__(256) void gn_apply_nchw_kernel(
+    const T* __restrict__ x, const float2* __restrict__ partial, int split,
+    const T* __restrict__ gamma, const T* __restrict__ beta, T* __restrict__ y, int C, int N,
+    float eps, int silu) {
+  __shared__ float2 coef;
+  const int c = blockIdx.y, b = blockIdx.z;
+  const int cg = C / kGroups;
+  const int g = b * kGroups + c / cg;
+  if (threadIdx.x < 64) {
+    double s1 = 0.0, s2 = 0.0;
+    for (int i = threadIdx.x; i < split; i += 64) {
+      const float2 pr = partial[g * split + i];
+      s1 += pr.x;
+      s2 += pr.y;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      s1 += __shfl_xor(s1, o, 64);
+      s2 += __shfl_xor(s2, o, 64);
+    }
+    if (threadIdx.x == 0) {
+      const double n = static_cast<double>(cg) * N;
+      const double shift = to_f32<T>(x[static_cast<long long>(g) * cg * N]);
+      const double dm = s1 / n;
+      double var = s2 / n - dm * dm;
+      if (var < 0.0) var = 0.0;
+      const float rstd = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
+      const float gm = gamma ? to_f32<T>(gamma[c]) : 1.f;
+      const float bt = beta ? to_f32<T>(beta[c]) : 0.f;
+      const float scale = rstd * gm;
+      coef = make_float2(scale, bt - static_cast<float>(shift + dm) * scale);
+    }
+  }
+  __syncthreads();
+  const float2 k = coef;
+  const long long plane = (static_cast<long long>(b) * C + c) * N;
+  const int n = blockIdx.x * 2048 + threadIdx.x * 8;
+  if (n >= N) return;
+  const T* src = x + plane + n;
+  T* dst = y + plane + n;
+  float v[8];
+  const bool vec = (N & 7) == 0;
+  if (vec) {
+    load8<T>(src, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = n + j < N ? to_f32<T>(src[j]) : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float a = fmaf(v[j], k.x, k.y);
+    if (silu) a = a / (1.0f + __expf(-a));
+    v[j] = a;
+  }
+  if (vec) {
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]),
+                                                  pack2bf(v[4], v[5]), pack2bf(v[6], v[7]));
+    } else {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (n + j < N) dst[j] = from_f32<T>(v[j]);
+  }
+}
+
+hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int max_split,
+                         const void* gamma, const void* beta, void* y, int B, int C, int N,
+                         float eps, bool silu, hipStream_t s) {
+  const int split = gn_split(C, N, max_split);
+  dim3 grid((N + 2047) / 2048, C, B);
+  if (bf16)
+    gn_apply_nchw_kernel<bf16_t><<<grid, 256, 0, s>>>(
+        static_cast<const bf16_t*>(x), partial, split, static_cast<const bf16_t*>(gamma),
+        static_cast<const bf16_t*>(beta), static_cast<bf16_t*>(y), C, N, eps, silu ? 1 : 0);
+  else
+    gn_apply_nchw_kernel<float><<<grid, 256, 0, s>>>(
+        static_cast<const float*>(x), partial, split, static_cast<const float*>(gamma),
+        static_cast<const float*>(beta), static_cast<float*>(y), C, N, eps, silu ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- guided DDPM step
+// x_prev = c1 * (x_t - c2 * eps) + sigma * z with eps = eps_u + scale *
+// (eps_c - eps_u), elementwise in fp32; eps_pair holds the unconditional
+// prediction in [0, n) and the conditional one in [n, 2n).
+template <typename TE>
+__global__ __launch_bounds__(256) void guided_ddpm_kernel(
+    const TE* __restrict__ eps_pair, const float* __restrict__ x_t,
+    const float* __restrict__ noise, float* __restrict__ x_prev, long long n, float scale,
+    float c1, float c2, float sigma) {
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float eu = to_f32<TE>(eps_pair[i]);
+    const float ec = to_f32<TE>(eps_pair[n + i]);
+    const float e = fmaf(scale, ec - eu, eu);
+    float v = c1 * fmaf(-c2, e, x_t[i]);
+    if (noise) v = fmaf(sigma, noise[i], v);
+    x_prev[i] = v;
+  }
+}
+
+hipError_t guided_ddpm(const void* eps_pair, bool eps_bf16, const float* x_t, const float* noise,
+                       float* x_prev, long long n, float scale, float c1, float c2, float sigma,
+                       hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (eps_bf16)
+    guided_ddpm_kernel<bf16_t><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        static_cast<const bf16_t*>(eps_pair), x_t, noise, x_prev, n, scale, c1, c2, sigma);
+  else
+    guided_ddpm_kernel<float><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        static_cast<const float*>(eps_pair), x_t, noise, x_prev, n, scale, c1, c2, sigma);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- LayerNorm
 // One wavefront per token row of the fp32 residual stream; the row, gamma and
 // beta are held in registers (VPL float4 each per lane), mean and variance

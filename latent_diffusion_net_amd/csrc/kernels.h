@@ -161,6 +161,17 @@ hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
                            int max_split, const float* gamma, const float* beta,
                            void* out, int out_type, int B, int C, int N,
                            int* range_flag, hipStream_t s);
+// GroupNorm apply NCHW -> NCHW from gn_stats partials, optionally followed
+// by SiLU; gamma/beta of the activation type (NULL = ones / zeros).
+hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int max_split,
+                         const void* gamma, const void* beta, void* y, int B, int C, int N,
+                         float eps, bool silu, hipStream_t s);
+// Guided DDPM step: x_prev[i] = c1 * (x_t[i] - c2 * e) + sigma * noise[i]
+// (noise NULL: no term), e = eps_u + scale * (eps_c - eps_u), eps_pair =
+// [eps_u (n); eps_c (n)] in bf16 or fp32; latents fp32.
+hipError_t guided_ddpm(const void* eps_pair, bool eps_bf16, const float* x_t, const float* noise,
+                       float* x_prev, long long n, float scale, float c1, float c2, float sigma,
+                       hipStream_t s);
 // u: [T][C] of type `out_type` (ACT_F32, ACT_BF16 or ACT_F16).
 hipError_t layernorm(const float* h, const float* gamma, const float* beta,
                      void* u, int out_type, int T, int C, hipStream_t s);

@@ -10,13 +10,16 @@ import pytest
 from latent_diffusion_net_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "st_block.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(st_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(st_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def _lib():
@@ -193,3 +196,36 @@ def test_null_handle_new_entry_points():
     d = ctypes.c_double()
     assert lib.st_measure_mfma_bf16(0, None, ctypes.byref(d), ctypes.byref(d)) \
         == binding.ST_ERR_INVALID
+
+
+def test_ops_validate_before_any_device_call():
+    """st_group_norm and st_guided_ddpm_step reject bad arguments with
+    ST_ERR_INVALID (no device needed: nothing is enqueued)."""
+    lib = _lib()
+    P = 0x10000
+    ws = lib.st_group_norm_workspace_bytes(2)
+    assert ws == 2 * 32 * 64 * 8
+    assert lib.st_group_norm_workspace_bytes(0) == 0
+    ok = dict(x=P, g=None, b=None, y=P + (1 << 30), B=2, C=64, H=4, W=4, eps=1e-5, silu=1,
+              dt=0, ws=P + (1 << 31), wsb=ws)
+
+    def gn(**kw):
+        a = dict(ok, **kw)
+        return lib.st_group_norm(a["x"], a["g"], a["b"], a["y"], a["B"], a["C"], a["H"], a["W"],
+                                 a["eps"], a["silu"], a["dt"], a["ws"], a["wsb"], None)
+    for kw, why in [(dict(x=None), "non-NULL"), (dict(B=0), "B"), (dict(C=48), "multiple of 32"),
+                    (dict(eps=0.0), "eps"), (dict(dt=5), "dtype"), (dict(x=P + 8), "aligned"),
+                    (dict(y=P + 64), "overlaps"), (dict(wsb=ws - 1), "workspace"),
+                    (dict(ws=None), "workspace")]:
+        assert gn(**kw) == binding.ST_ERR_INVALID, kw
+        assert why in binding.last_error(), (kw, binding.last_error())
+
+    def dd(**kw):
+        a = dict(eps=P, dt=0, xt=P, z=None, xp=P, n=16, s=7.5, t=10, T=1000, b0=1e-4, b1=0.02)
+        a.update(kw)
+        return lib.st_guided_ddpm_step(a["eps"], a["dt"], a["xt"], a["z"], a["xp"], a["n"], a["s"],
+                                       a["t"], a["T"], a["b0"], a["b1"], None)
+    for kw in [dict(t=0), dict(t=1001), dict(T=0), dict(n=-1), dict(b0=0.0), dict(b1=1.0),
+               dict(dt=3), dict(eps=None), dict(s=float("inf"))]:
+        assert dd(**kw) == binding.ST_ERR_INVALID, kw
+    assert dd(n=0, eps=None, xt=None, xp=None) == binding.ST_OK  # nothing to do
