@@ -52,6 +52,21 @@ st_status st_group_norm(const void *x, const void *gamma, const void *beta, void
                         void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as st_group_norm, with the partial sums in a static 1 MiB
+ * device array of the library (one per GPU, held until the process ends)
+ * instead of a caller workspace.  It calls no allocating routine.  B <= 64
+ * (larger: ST_ERR_UNSUPPORTED, nothing enqueued).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race on it, so they must be serialised; sequential
+ * calls need no clearing (each call writes every slot it reads).
+ */
+st_status st_group_norm_noalloc(const void *x, const void *gamma, const void *beta,
+                                void *y, int B, int C, int H, int W, float eps, int silu,
+                                st_dtype dtype, void *stream);
+
+/*
  * Guided DDPM step for one classifier-free-guidance pair:
  *   eps      = eps_u + guidance_scale * (eps_c - eps_u)
  *   x_prev   = 1/sqrt(alpha_t) * (x_t - beta_t / sqrt(1 - alphabar_t) * eps)

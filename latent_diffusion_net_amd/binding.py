@@ -37,7 +37,8 @@ EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_stage",
            "st_block_destroy", "st_block_check_range", "st_last_error",
            "st_block_set_timing", "st_block_read_timing",
            "st_block_read_timing_launches", "st_measure_mfma_bf16",
-           "st_group_norm_workspace_bytes", "st_group_norm", "st_guided_ddpm_step")
+           "st_group_norm_workspace_bytes", "st_group_norm", "st_group_norm_noalloc",
+           "st_guided_ddpm_step")
 
 
 class LayerWeights(ctypes.Structure):
@@ -109,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_group_norm_workspace_bytes.restype = sz
     lib.st_group_norm.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp, sz, vp]
     lib.st_group_norm.restype = i
+    lib.st_group_norm_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp]
+    lib.st_group_norm_noalloc.restype = i
     lib.st_guided_ddpm_step.argtypes = [vp, i, vp, vp, vp, ll, f32, i, i, dbl, dbl, vp]
     lib.st_guided_ddpm_step.restype = i
     _lib = lib
@@ -257,6 +260,17 @@ def group_norm(x, gamma=None, beta=None, eps: float = 1e-5, silu: bool = False,
     _check(lib.st_group_norm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), B, C, H, W, eps,
                              1 if silu else 0, _dtype_code(x), _ptr(workspace), nbytes,
                              _stream_handle(stream)))
+    return y
+
+
+def group_norm_noalloc(x, y, gamma=None, beta=None, eps: float = 1e-5, silu: bool = False,
+                       stream=None):
+    """st_group_norm_noalloc: as group_norm, partial sums in the library's
+    static device array (no allocation; ``y`` must be given)."""
+    lib = load_library()
+    B, C, H, W = x.shape
+    _check(lib.st_group_norm_noalloc(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), B, C, H, W, eps,
+                                     1 if silu else 0, _dtype_code(x), _stream_handle(stream)))
     return y
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "../../include/st_ops.h"
@@ -57,7 +58,56 @@ st_status run_gn(const void* x, const void* gamma, const void* beta, void* y, in
   return ST_OK;
 }
 
+// Allocation-free GroupNorm: the partial sums live in this file-scope
+// device array (one copy per GPU, held until the process ends) instead of
+// a caller workspace.  1 MiB: B <= 64 samples of 32 groups x 64 slices.
+// Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in for the symbol): it passes the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in g_scratch_dev.
+constexpr int kScratchMaxBatch = 64;
+constexpr int kScratchPartials = kScratchMaxBatch * ST_GN_GROUPS * kGnMaxSplit;
+static __device__ __align__(256) float2 scratch[kScratchPartials];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float2* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+st_status scratch_on_current_device(float2** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ST_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ST_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ST_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<float2*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return ST_OK;
+}
+
 }  // namespace
+
+ST_API st_status st_group_norm_noalloc(const void* x, const void* gamma, const void* beta,
+                                       void* y, int B, int C, int H, int W, float eps, int silu,
+                                       st_dtype dtype, void* stream) {
+  st_set_error(ST_OK, "");
+  st_status st = check_gn(x, y, B, C, H, W, eps, dtype);
+  if (st != ST_OK) return st;
+  if (B > kScratchMaxBatch)
+    return fail(ST_ERR_UNSUPPORTED, "st_group_norm_noalloc: B must be <= 64 (static scratch of 1 MiB)");
+  float2* part = nullptr;
+  st = scratch_on_current_device(&part);
+  if (st != ST_OK) return st;
+  // every slot the statistics pass writes is read back by the apply pass of
+  // the same call: nothing needs clearing
+  return run_gn(x, gamma, beta, y, B, C, H, W, eps, silu, dtype, part, static_cast<hipStream_t>(stream));
+}
 
 ST_API size_t st_group_norm_workspace_bytes(int B) {
   return B > 0 ? static_cast<size_t>(B) * ST_GN_GROUPS * kGnMaxSplit * sizeof(float2) : 0;
