@@ -147,6 +147,21 @@ st_status st_block_forward(st_block *blk, const void *x, const void *ctx,
                            void *y, void *stream);
 
 /*
+ * st_block_forward with a key padding mask on the context ("企业官网建设流程全解析"
+ * §5.5, Cross-Attention mask: the tokenizer's attention_mask, 0 marking a
+ * padding token that must take no part in the cross-attention).
+ *   ctx_mask [B][77] device bytes, nonzero = a real token (attended), 0 =
+ *            padding (excluded from the softmax of every cross-attention);
+ *            NULL = no mask (exactly st_block_forward).  A sample whose
+ *            every token is masked gets a zero cross-attention output.
+ * Other arguments, validation and errors as st_block_forward; ctx_mask is
+ * read on the stream and must stay valid until the stream reaches it; y
+ * must not overlap it.
+ */
+st_status st_block_forward_masked(st_block *blk, const void *x, const void *ctx,
+                                  const unsigned char *ctx_mask, void *y, void *stream);
+
+/*
  * Debug: run the forward up to `stage` and copy the fp32 residual stream h
  * ([T][C], token n = i*W + j of sample b at row b*N + n) to `h_out` (device,
  * T*C floats).  stage 0 = after proj_in; stage 1 + 3*l + s = after sublayer

@@ -33,7 +33,8 @@ BLOCK_FIELDS = ("gn_w", "gn_b", "proj_in_w", "proj_in_b", "proj_out_w",
                 "proj_out_b")
 
 # Every function include/st_block.h and include/st_ops.h declare.
-EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_stage",
+EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_masked",
+           "st_block_forward_stage",
            "st_block_destroy", "st_block_check_range", "st_last_error",
            "st_block_set_timing", "st_block_read_timing",
            "st_block_read_timing_launches", "st_measure_mfma_bf16",
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_block_create.restype = i
     lib.st_block_forward.argtypes = [vp, vp, vp, vp, vp]
     lib.st_block_forward.restype = i
+    lib.st_block_forward_masked.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.st_block_forward_masked.restype = i
     lib.st_block_forward_stage.argtypes = [vp, vp, vp, i, vp, vp]
     lib.st_block_forward_stage.restype = i
     lib.st_block_destroy.argtypes = [vp]
@@ -184,6 +187,16 @@ class STBlock:
             y = torch.empty_like(x)
         _check(self._lib.st_block_forward(self._h, _ptr(x), _ptr(ctx), _ptr(y),
                                           _stream_handle(stream)))
+        return y
+
+    def forward_masked(self, x, ctx, ctx_mask, y=None, stream=None):
+        """y = block(x, ctx) with the context key padding mask ``ctx_mask``
+        ([B, 77] uint8 device tensor, nonzero = attend; None = no mask)."""
+        import torch
+        if y is None:
+            y = torch.empty_like(x)
+        _check(self._lib.st_block_forward_masked(self._h, _ptr(x), _ptr(ctx), _ptr(ctx_mask),
+                                                 _ptr(y), _stream_handle(stream)))
         return y
 
     def forward_stage(self, x, ctx, stage: int, stream=None):

@@ -132,6 +132,8 @@ struct st_block {
   // (the residual stream, the GEGLU output or the normalised input); read
   // and cleared by st_block_check_range
   int* range_flag;
+  // context key padding mask of the current forward as bits, [B][4] words
+  uint32_t* key_bits;
 
   unsigned timing_mask;
   std::vector<PendingTiming> pending;
@@ -298,6 +300,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   if (const char* cap = std::getenv("ST_MAX_DEVICE_BYTES")) b->bytes_cap = std::strtoull(cap, nullptr, 10);
   b->timing_mask = 0;
   b->range_flag = nullptr;
+  b->key_bits = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Creator cr{b, s};
@@ -470,6 +473,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
           "self-attention partial results"));
     }
   }
+  b->key_bits = static_cast<uint32_t*>(cr.alloc(sizeof(uint32_t) * 4 * B, "context key mask"));
   b->kc = cr.alloc(b->ctx_layer_stride * depth * es, "context K");
   b->vct = cr.alloc(b->ctx_layer_stride * depth * es, "context V^T");
   // Padding rows of the per-head buffers are read by the attention kernels
@@ -559,8 +563,8 @@ GemmParams gemm(const void* A, long long lda, const void* Bm, long long ldb,
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
-                       int stop_stage, float* h_out, hipStream_t s) {
+st_status forward_impl(st_block* b, const void* x, const void* ctx, const uint8_t* ctx_mask,
+                       void* y, int stop_stage, float* h_out, hipStream_t s) {
   const bool bf = b->bf16;
   const int B = b->B, C = b->C, N = b->N, T = b->T, F = b->F, D = b->D;
   // 16-bit path operand types: fp16 where an activation produced by a norm
@@ -603,6 +607,12 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
     p.epi.ln_blocks = C / 64; p.epi.ln_eps = kLayerNormEps;
   };
 
+  // the context's key padding mask as bits (read by every cross-attention)
+  const uint32_t* key_bits = nullptr;
+  if (ctx_mask) {
+    ST_TRY(mask_to_bits(ctx_mask, b->key_bits, B, ST_CTX_LEN, s), "context key mask");
+    key_bits = b->key_bits;
+  }
   ST_TRY(run(b, ST_K_GN_STATS, s, [&] {
            return gn_stats(x, bf, B, C, N, b->gn_part, b->gn_max_split, s);
          }), "GroupNorm statistics");
@@ -688,6 +698,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
                p.epi.ca.kv_pad = b->cpad; p.epi.ca.nk = ST_CTX_LEN;
                p.epi.ca.rows_per_batch = N; p.epi.ca.heads = b->heads;
                p.epi.ca.scale = attention_bf16_q_scale();
+               p.epi.ca.key_bits = key_bits;
                return G(p, ACT_F16);
              }
              p.epi.hs.dst[0] = b->q; p.epi.hs.dst[1] = nullptr; p.epi.hs.dst[2] = nullptr;
@@ -705,6 +716,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, void* y,
              a.o = b->o;
              a.B = B; a.heads = b->heads; a.C = C; a.Nq = N; a.Nk = ST_CTX_LEN;
              a.q_pad = b->npad; a.kv_pad = b->cpad;
+             a.key_bits = key_bits;
              return bf ? attention_bf16(a, s) : attention_f32(a, s);
            }), "cross-attention");
     ST_TRY(run(b, ST_K_ATTN_OUT, s, [&] {
@@ -805,7 +817,21 @@ ST_API st_status st_block_forward(st_block* b, const void* x, const void* ctx,
   if (st != ST_OK) return st;
   DeviceGuard g(b->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "select device");
-  return forward_impl(b, x, ctx, y, -1, nullptr, static_cast<hipStream_t>(stream));
+  return forward_impl(b, x, ctx, nullptr, y, -1, nullptr, static_cast<hipStream_t>(stream));
+}
+
+ST_API st_status st_block_forward_masked(st_block* b, const void* x, const void* ctx,
+                                         const unsigned char* ctx_mask, void* y, void* stream) {
+  g_err.clear();
+  st_status st = check_forward_args(b, x, ctx, y);
+  if (st != ST_OK) return st;
+  if (ctx_mask && overlaps(y, static_cast<size_t>(b->T) * b->C * b->esz, ctx_mask,
+                           static_cast<size_t>(b->B) * ST_CTX_LEN))
+    return fail(ST_ERR_INVALID, "y overlaps ctx_mask");
+  DeviceGuard g(b->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "select device");
+  return forward_impl(b, x, ctx, reinterpret_cast<const uint8_t*>(ctx_mask), y, -1, nullptr,
+                      static_cast<hipStream_t>(stream));
 }
 
 ST_API st_status st_block_forward_stage(st_block* b, const void* x,
@@ -819,7 +845,7 @@ ST_API st_status st_block_forward_stage(st_block* b, const void* x,
   if (stage < 0 || stage > 3 * b->depth) return fail(ST_ERR_INVALID, "stage out of range");
   DeviceGuard g(b->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "select device");
-  return forward_impl(b, x, ctx, nullptr, stage, h_out, static_cast<hipStream_t>(stream));
+  return forward_impl(b, x, ctx, nullptr, nullptr, stage, h_out, static_cast<hipStream_t>(stream));
 }
 
 ST_API void st_block_destroy(st_block* b) {

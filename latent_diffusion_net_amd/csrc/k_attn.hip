@@ -322,6 +322,35 @@ __global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16
           if (perm(kb * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3)) >= kvalid) sc[qb][kb][r] = -INFINITY;
   };
 
+  // Cross-attention with a key padding mask: masked keys of tile t get a
+  // finite score far below any real one (-30000 in base-2 units), not -inf,
+  // so that a tile with every key masked still has a finite maximum; the
+  // lazy-max rescale then scales its contributions to exactly 0 as soon as a
+  // real key appears, and a sample with no real key is zeroed at the store.
+  uint32_t kbw[4] = {~0u, ~0u, ~0u, 0u};
+  bool any_key = true;
+  if constexpr (KIND == 1) {
+    if (p.key_bits) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p.key_bits + 4LL * b);
+      kbw[0] = w.x; kbw[1] = w.y; kbw[2] = w.z; kbw[3] = w.w;
+      any_key = (w.x | w.y | w.z | w.w) != 0u;
+    }
+  }
+  auto mask_keys = [&](int t, floatx16 (&sc)[QB][2]) {
+    if constexpr (KIND == 1) {
+      if (!p.key_bits || t > 1) return;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t wd = t == 0 ? kbw[kb] : kbw[2 + kb];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((wd >> perm(8 * (r >> 2) + 4 * lhi + (r & 3))) & 1u)) sc[qb][kb][r] = -30000.f;
+        }
+    }
+  };
+
   // Software pipeline over key tiles.  Iteration t turns S_t into P_t on the
   // vector units, computes S_{t+1} in the registers that S_t held, then adds
   // P_t V_t.  Tile j of K and of V^T lives in buffer j % 3: iteration t reads
@@ -341,6 +370,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16
   wait_vmcnt_lds<0>();
   stage_barrier();
   qk(sK0, sc);
+  mask_keys(kt0, sc);
   if (ragged_last == kt0) mask_tile(kt0, sc);
   first_max(sc);
   stage_barrier();  // every wavefront is done with K_0 before K_3 replaces it
@@ -361,6 +391,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16
     // S_{t+1} (unused past the last tile: its LDS buffer then holds stale,
     // finite data)
     qk(kn, sc);
+    mask_keys(kt0 + t + 1, sc);
     if (kt0 + t + 1 == ragged_last) mask_tile(kt0 + t + 1, sc);
     pv(vc, pb);
     // K_{t+2} and V_{t+1} have landed (loads complete in order, so at most
@@ -414,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16
   // Whole tile: normalise, store O[token][head*64 + d].
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.0f / l_tot[qb];
+    const float inv = any_key ? 1.0f / l_tot[qb] : 0.f;
     const int qrow = q0 + qb * 32 + l32;
     if (qrow < p.Nq) {
       uint16_t* orow = static_cast<uint16_t*>(p.o) +
@@ -533,6 +564,7 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(AttnParams p) {
     __syncthreads();
     const int kn = min(FKT, p.Nk - k0);
     for (int j = 0; j < kn; ++j) {
+      if (p.key_bits && !((p.key_bits[4 * b + ((k0 + j) >> 5)] >> ((k0 + j) & 31)) & 1u)) continue;
       float s = 0.f;
       for (int d = 0; d < 64; ++d) s = fmaf(q[d], sK[j][d], s);
       s *= 0.125f;
@@ -546,7 +578,7 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(AttnParams p) {
   }
   if (qi < p.Nq) {
     float* orow = static_cast<float*>(p.o) + (static_cast<long long>(b) * p.Nq + qi) * p.C + head * 64;
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;  // every key masked: O = 0
     for (int d = 0; d < 64; ++d) orow[d] = o[d] * inv;
   }
 }
@@ -600,6 +632,7 @@ hipError_t attention_bf16(const AttnParams& p, hipStream_t s) {
   if (p.q_pad < qtiles * kQT || p.kv_pad < ((p.Nk + KT - 1) / KT) * KT)
     return hipErrorInvalidValue;  // padded buffers must cover every tile
   int grid = tiles;
+  if (p.key_bits && (p.Nk > 96 || p.nsplit > 1)) return hipErrorInvalidValue;
   if (p.nsplit > 1) {
     if (!p.part || p.n_full < 0 || p.n_full >= tiles || (p.Nk + KT - 1) / KT < p.nsplit)
       return hipErrorInvalidValue;

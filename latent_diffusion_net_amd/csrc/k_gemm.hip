@@ -115,7 +115,12 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
   const int l32 = lane & 31, lhi = lane >> 5;
   const CrossAttn& ca = p.epi.ca;
   if (R0 >= p.M || C0 >= p.N) return;
-  const long long bh = static_cast<long long>(R0 / ca.rows_per_batch) * ca.heads + (C0 >> 6);
+  const int sample = R0 / ca.rows_per_batch;
+  const long long bh = static_cast<long long>(sample) * ca.heads + (C0 >> 6);
+  // key padding mask of this sample (all keys below nk when there is none)
+  uint4 kbits = make_uint4(~0u, ~0u, ~0u, 0u);
+  if (ca.key_bits) kbits = *reinterpret_cast<const uint4*>(ca.key_bits + 4LL * sample);
+  const uint32_t kbw[3] = {kbits.x, kbits.y, kbits.z};
   const uint16_t* Kh = static_cast<const uint16_t*>(ca.k) + bh * ca.kv_pad * kHeadDim;
   const uint16_t* Vh = static_cast<const uint16_t*>(ca.vt) + bh * kHeadDim * ca.kv_pad;
   uint4 kop[3][4], vop[2][6];
@@ -184,16 +189,19 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) sc[kb] = mfma32x32x16(kop[kb][s4], qop[s4], sc[kb], bf16_t{});
     }
-    // keys >= nk (nk > 64: only the third block has any) -> -inf
+    // keys >= nk (nk > 64: only the third block has any) and masked keys
+    // -> -inf
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (kb == 2 && 64 + kperm(8 * (r >> 2) + 4 * lhi + (r & 3)) >= ca.nk) sc[kb][r] = -INFINITY;
+        const int kr = kperm(8 * (r >> 2) + 4 * lhi + (r & 3));
+        if ((kb == 2 && 64 + kr >= ca.nk) || !((kbw[kb] >> kr) & 1u)) sc[kb][r] = -INFINITY;
         mx = fmaxf(mx, sc[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx == -INFINITY) mx = 0.f;  // every key masked: all probabilities 0
     // P^T step st: block st / 2, entries 8 (st % 2) + 0..7 = keys 16 st + 8 lhi + 0..7;
     // steps past the last key are zero and skipped
     const int nsteps = (ca.nk + 15) >> 4;
@@ -216,7 +224,8 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
       }
       pb[st] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    const float inv = 1.0f / (ps + __shfl_xor(ps, 32, 64));
+    const float ptot = ps + __shfl_xor(ps, 32, 64);
+    const float inv = ptot > 0.f ? 1.0f / ptot : 0.f;  // no key: O = 0
     floatx16 o[2];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {

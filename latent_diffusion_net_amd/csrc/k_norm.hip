@@ -307,6 +307,29 @@ hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int ma
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- key padding mask
+__global__ __launch_bounds__(64) void mask_to_bits_kernel(const uint8_t* __restrict__ mask,
+                                                          uint32_t* __restrict__ bits, int nk) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  // lane k < 32 covers keys k, 32 + k, 64 + k
+  uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int key = 32 * i + lane;
+    const bool on = lane < 32 && key < nk && mask[static_cast<long long>(b) * nk + key] != 0;
+    w[i] = static_cast<uint32_t>(__ballot(on));  // lanes 0..31 of the ballot
+  }
+  if (lane == 0)
+    *reinterpret_cast<uint4*>(bits + 4LL * b) = make_uint4(w[0], w[1], w[2], 0u);
+}
+
+hipError_t mask_to_bits(const uint8_t* mask, uint32_t* bits, int B, int nk, hipStream_t s) {
+  if (nk > 96) return hipErrorInvalidValue;
+  mask_to_bits_kernel<<<B, 64, 0, s>>>(mask, bits, nk);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------- guided DDPM step
 // x_prev = c1 * (x_t - c2 * eps) + sigma * z with eps = eps_u + scale *
 // (eps_c - eps_u), elementwise in fp32; eps_pair holds the unconditional

@@ -27,12 +27,16 @@ enum EpiKind {
 // keys (64 < nk <= 96) of k [B*heads][kv_pad][64] and vt [B*heads][64][kv_pad] (bf16,
 // kv_pad >= 96, padding finite) with softmax base 2 (scale includes
 // log2(e)); O goes to o [M][ldo] bf16, columns as in the product.
+// key_bits (may be NULL): the context's key padding mask, 4 words per
+// sample, bit k of word w set when key 32 w + k attends; a sample with no
+// bit set gets O = 0.
 struct CrossAttn {
   const void* k;
   const void* vt;
   int kv_pad, nk;
   int rows_per_batch, heads;
   float scale;
+  const uint32_t* key_bits;
 };
 
 // Destination of the head-split epilogue.  Column col of the product maps to
@@ -131,6 +135,9 @@ struct AttnParams {
   // second kernel merges them in piece order.  nsplit <= 1: no split.
   int n_full, nsplit;
   float* part;        // [tiles - n_full][nsplit][attention_bf16_part_floats()]
+  // Cross-attention only (Nk <= 96, no split): key padding mask as in
+  // CrossAttn::key_bits, or NULL.
+  const uint32_t* key_bits;
 };
 // bf16 path: q holds the queries already multiplied by
 // attention_bf16_q_scale() = log2(e) / sqrt(64), so that the kernel's scores
@@ -166,6 +173,9 @@ hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
 hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int max_split,
                          const void* gamma, const void* beta, void* y, int B, int C, int N,
                          float eps, bool silu, hipStream_t s);
+// Key padding mask [B][nk] bytes (nonzero = attend) -> bits [B][4] words
+// (bit k of word w: key 32 w + k; keys >= nk clear); nk <= 96.
+hipError_t mask_to_bits(const uint8_t* mask, uint32_t* bits, int B, int nk, hipStream_t s);
 // Guided DDPM step: x_prev[i] = c1 * (x_t[i] - c2 * e) + sigma * noise[i]
 // (noise NULL: no term), e = eps_u + scale * (eps_c - eps_u), eps_pair =
 // [eps_u (n); eps_c (n)] in bf16 or fp32; latents fp32.

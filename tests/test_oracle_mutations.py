@@ -109,12 +109,12 @@ def _sa_no_residual(h, lw, heads):
     return ob.linear(ob.attention(q, k, v, heads), lw["o1_w"], lw.get("o1_b"))
 
 
-def _ca_normalised_context(h, ctx, lw, heads):
+def _ca_normalised_context(h, ctx, lw, heads, ctx_mask=None):
     u = ob.layer_norm(h, lw["ln2_w"], lw["ln2_b"])
     c = ob.layer_norm(ctx, np.ones(ctx.shape[-1]), np.zeros(ctx.shape[-1]))
     q = ob.linear(u, lw["q2_w"], lw.get("q2_b"))
     o = ob.attention(q, ob.linear(c, lw["k2_w"], lw.get("k2_b")),
-                     ob.linear(c, lw["v2_w"], lw.get("v2_b")), heads)
+                     ob.linear(c, lw["v2_w"], lw.get("v2_b")), heads, key_mask=ctx_mask)
     return h + ob.linear(o, lw["o2_w"], lw.get("o2_b"))
 
 

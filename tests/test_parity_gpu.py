@@ -395,3 +395,74 @@ def test_fp16_stream_overflow_is_reported():
         if not expect:
             assert torch.isfinite(y.float()).all()
         blk.close()
+
+
+def _masks(B, kind):
+    m = np.ones((B, 77), np.uint8)
+    if kind == "padded":        # tokenizer padding: real tokens first
+        for b in range(B):
+            m[b, 12 + 9 * b:] = 0
+    elif kind == "scattered":
+        m[:, 3::4] = 0
+        m[-1, :70] = 0
+    elif kind == "first_tile_masked":  # every key of the first 64 masked
+        m[:, :64] = 0
+    elif kind == "one_sample_empty":   # the last sample has no real token
+        m[0, 40:] = 0
+        m[-1, :] = 0
+    return m
+
+
+MASK_CASES = [
+    # bf16, H*W % 64 == 0: cross-attention in the cross-Q epilogue
+    ("fused", synth.BlockConfig("mask_fused", 2, 128, 8, 8, 2, 128, 2, "bf16")),
+    # bf16, H*W = 225: the separate 77-key attention kernel (128-query tiles)
+    ("kernel", synth.BlockConfig("mask_kernel", 2, 128, 15, 15, 2, 128, 2, "bf16")),
+    # fp32 path
+    ("f32", synth.BlockConfig("mask_f32", 2, 128, 15, 15, 2, 128, 2, "f32")),
+]
+
+
+@pytest.mark.parametrize("kind", ["padded", "scattered", "first_tile_masked", "one_sample_empty"])
+@pytest.mark.parametrize("path,cfg", MASK_CASES, ids=[c[0] for c in MASK_CASES])
+def test_cross_attention_key_mask(path, cfg, kind):
+    """st_block_forward_masked against the oracle with the same key padding
+    mask (anatomy article §5.5), on every cross-attention path; a softmax
+    far from flat (logit std ~3 in both attentions), so that the mask
+    visibly matters; an all-ones mask equals the unmasked forward bitwise."""
+    import math
+    import torch
+    from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
+    inp = synth.make_inputs(cfg, 61, bias_std=0.05, norm_std=0.2, qk_std=math.sqrt(3.0 / cfg.C))
+    m = _masks(cfg.B, kind)
+    _say(f"[gpu] key mask {path} {kind}: B={cfg.B} C={cfg.C} N={cfg.N} dtype={cfg.dtype}")
+    p = params_to_device(inp["params"], cfg.dtype)
+    x = array_to_device(inp["x"], cfg.dtype)
+    ctx = array_to_device(inp["ctx"], cfg.dtype)
+    blk = STBlock(cfg.B, cfg.C, cfg.H, cfg.W, cfg.heads, cfg.D_ctx, cfg.depth, cfg.dtype, p)
+    md = torch.from_numpy(m).cuda()
+    y = blk.forward_masked(x, ctx, md)
+    y1 = blk.forward_masked(x, ctx, torch.ones_like(md))
+    y0 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16 if cfg.dtype == "bf16" else torch.int32),
+                       y0.view(torch.int16 if cfg.dtype == "bf16" else torch.int32))
+    y = y.float().cpu().numpy().astype(np.float64)
+    blk.close()
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads, ctx_mask=m)
+    yu = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    x64 = np.asarray(inp["x"], np.float64)
+    moved = rel_l2(yo - x64, yu - x64)
+    _say(f"    the mask moves the oracle's update by {moved:.3e} (rel-L2)")
+    assert moved > 0.05
+    check(cfg, inp, y, yo)
+
+
+def test_refiner_depth_four():
+    """Depth 4 (the SDXL Refiner's transformer depth) at a Refiner-like stage:
+    C = 768, 32 x 32, context width 1280 (OpenCLIP ViT-bigG)."""
+    cfg = synth.BlockConfig("refiner_c768_32x32_d4", 2, 768, 32, 32, 12, 1280, 4, "bf16")
+    inp = synth.make_inputs(cfg, 71, bias_std=0.02, norm_std=0.1)
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    y, _ = run_gpu(cfg, inp)
+    check(cfg, inp, y, yo)
