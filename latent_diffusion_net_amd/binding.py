@@ -39,7 +39,8 @@ EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_masked",
            "st_block_set_timing", "st_block_read_timing",
            "st_block_read_timing_launches", "st_measure_mfma_bf16",
            "st_group_norm_workspace_bytes", "st_group_norm", "st_group_norm_noalloc",
-           "st_guided_ddpm_step")
+           "st_guided_ddpm_step", "st_resnet_create", "st_resnet_forward",
+           "st_resnet_check_range", "st_resnet_destroy")
 
 
 class LayerWeights(ctypes.Structure):
@@ -49,6 +50,14 @@ class LayerWeights(ctypes.Structure):
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [
         ("layers", ctypes.POINTER(LayerWeights))]
+
+
+RESNET_FIELDS = ("gn1_w", "gn1_b", "conv1_w", "conv1_b", "temb_w", "temb_b", "gn2_w",
+                 "gn2_b", "conv2_w", "conv2_b", "sc_w", "sc_b")
+
+
+class ResnetWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in RESNET_FIELDS]
 
 
 class Timing(ctypes.Structure):
@@ -113,6 +122,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_group_norm_workspace_bytes.restype = sz
     lib.st_group_norm.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp, sz, vp]
     lib.st_group_norm.restype = i
+    lib.st_resnet_create.argtypes = [i, i, i, i, i, i, f32, i, ctypes.POINTER(ResnetWeights), vp,
+                                     ctypes.POINTER(vp)]
+    lib.st_resnet_create.restype = i
+    lib.st_resnet_forward.argtypes = [vp, vp, vp, vp, vp]
+    lib.st_resnet_forward.restype = i
+    lib.st_resnet_check_range.argtypes = [vp, vp]
+    lib.st_resnet_check_range.restype = i
+    lib.st_resnet_destroy.argtypes = [vp]
+    lib.st_resnet_destroy.restype = None
     lib.st_group_norm_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp]
     lib.st_group_norm_noalloc.restype = i
     lib.st_guided_ddpm_step.argtypes = [vp, i, vp, vp, vp, ll, f32, i, i, dbl, dbl, vp]
@@ -238,6 +256,48 @@ class STBlock:
     def close(self):
         if self._h is not None:
             self._lib.st_block_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class STResnet:
+    """One ResnetBlock2D (owns a library handle).  ``params``: device bf16
+    tensors named as ``RESNET_FIELDS`` (biases, gammas and betas optional;
+    sc_w / sc_b only when Cin != Cout).  The library copies the weights."""
+
+    def __init__(self, B, Cin, Cout, H, W, Dt, params: Dict, eps: float = 1e-5, stream=None):
+        self._lib = load_library()
+        self._h = None
+        self.shape = (B, Cin, Cout, H, W, Dt)
+        w = ResnetWeights()
+        for n in RESNET_FIELDS:
+            setattr(w, n, _ptr(params.get(n)))
+        handle = ctypes.c_void_p()
+        _check(self._lib.st_resnet_create(B, Cin, Cout, H, W, Dt, eps, ST_DTYPE_BF16,
+                                          ctypes.byref(w), _stream_handle(stream),
+                                          ctypes.byref(handle)))
+        self._h = handle
+
+    def forward(self, x, temb, y=None, stream=None):
+        import torch
+        B, Cin, Cout, H, W, Dt = self.shape
+        if y is None:
+            y = torch.empty((B, Cout, H, W), dtype=x.dtype, device=x.device)
+        _check(self._lib.st_resnet_forward(self._h, _ptr(x), _ptr(temb), _ptr(y),
+                                           _stream_handle(stream)))
+        return y
+
+    def check_range(self, stream=None):
+        _check(self._lib.st_resnet_check_range(self._h, _stream_handle(stream)))
+
+    def close(self):
+        if self._h is not None:
+            self._lib.st_resnet_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -528,6 +528,51 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
         }
       }
     }
+  } else if constexpr (EPI == EPI_CONV) {
+    // rows = output channels, columns = output pixels m of the padded grid
+    // (m = (b * Hq + i) * Wp + j; valid when i < Ho and j < Wo): y[b][c][i][j]
+    // = acc + cadd[b][c] (+ resid[b][c][i][j]); lane -> 4 consecutive pixels
+    // of one channel, 16 channels per pass.  Wp % 4 == 0 and Wo % 4 == 0
+    // keep a group of four in one row, all valid or all padding.
+    const ConvGemm& cv = p.conv;
+    const int lc = (lane & 15) * 4;
+    const int m0 = C0 + lc;
+    const int per_b = cv.Hq * cv.Wp;
+    const int b = m0 / per_b;
+    const int rem = m0 - b * per_b;
+    const int i = rem / cv.Wp;
+    const int j = rem - i * cv.Wp;
+    if (m0 >= N || i >= cv.Ho || j >= cv.Wo) return;
+    const long long plane = static_cast<long long>(cv.Ho) * cv.Wo;
+    const long long pix = static_cast<long long>(i) * cv.Wo + j;
+    const bf16_t* rin = static_cast<const bf16_t*>(cv.resid);
+    bf16_t* yout = static_cast<bf16_t*>(cv.out);
+    uint2 rv[16];
+    if (rin) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int c = R0 + it * 4 + (lane >> 4);
+        rv[it] = c < M ? *reinterpret_cast<const uint2*>(rin + (static_cast<long long>(b) * M + c) * plane + pix)
+                       : make_uint2(0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int lr = it * 4 + (lane >> 4);
+      const int c = R0 + lr;
+      if (c >= M) break;
+      const float add = cv.cadd[static_cast<long long>(b) * M + c];
+      const float4 a = *reinterpret_cast<const float4*>(&stage[stg(lr, lc)]);
+      float y0 = a.x + add, y1 = a.y + add, y2 = a.z + add, y3 = a.w + add;
+      if (rin) {
+        y0 += __uint_as_float(rv[it].x << 16);
+        y1 += __uint_as_float(rv[it].x & 0xffff0000u);
+        y2 += __uint_as_float(rv[it].y << 16);
+        y3 += __uint_as_float(rv[it].y & 0xffff0000u);
+      }
+      *reinterpret_cast<uint2*>(yout + (static_cast<long long>(b) * M + c) * plane + pix) =
+          make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
+    }
   } else if constexpr (EPI == EPI_NCHW) {
     // rows = channels, columns = tokens: y[b][c][n] = acc + bias[c] + x[b][c][n];
     // lane -> 4 consecutive tokens of one channel
@@ -669,14 +714,36 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     const int cl = (lane & 7) ^ ((row >> 1) & 7);
     boff[j2] = static_cast<unsigned>((min(n0 + row, N - 1) * p.ldb + kz * kslice + cl * 8) * 2);
   }
-  const int abytes = M * static_cast<int>(p.lda) * 2, bbytes = N * static_cast<int>(p.ldb) * 2;
+  const int abytes = M * static_cast<int>(p.lda) * 2;
+  const int bbytes = EPI == EPI_CONV ? static_cast<int>(p.conv.b_bytes) : N * static_cast<int>(p.ldb) * 2;
+  // Convolution: the byte offset of K stage k within the activation buffer,
+  // tracked incrementally (every caller asks for the stages in order, one
+  // at a time): tap ct = 3 di + dj at (crow, ccol), stage cj of the tap.
+  int ct = 0, cj = 0, crow = 0, ccol = 0;
+  auto next_boff = [&](int k) -> int {
+    if constexpr (EPI != EPI_CONV) {
+      return k * BKT * 2;
+    } else {
+      const ConvGemm& cv = p.conv;
+      int off;
+      if (ct < 9) off = ((crow * cv.Wp + ccol) * cv.L + cj * BKT) * 2;
+      else off = (cv.sc_roff * cv.L + cv.sc_cbase + cj * BKT) * 2;
+      if (++cj == (ct < 9 ? cv.spt : cv.sc_spt)) {
+        cj = 0;
+        ++ct;
+        if (++ccol == 3) { ccol = 0; ++crow; }
+      }
+      return off;
+    }
+  };
   auto issue = [&](int k, uint16_t* sa, uint16_t* sb) {
+    const int bk = next_boff(k);
 #pragma unroll
     for (int j2 = 0; j2 < DPA; ++j2)
       dma16(A, abytes, sa + (wave * DPA + j2) * 512, aoff[j2], k * BKT * 2);
 #pragma unroll
     for (int j2 = 0; j2 < DPB; ++j2)
-      dma16(Bm, bbytes, sb + (wave * DPB + j2) * 512, boff[j2], k * BKT * 2);
+      dma16(Bm, bbytes, sb + (wave * DPB + j2) * 512, boff[j2], bk);
   };
 
   floatx16 acc[FM][FN];
@@ -770,11 +837,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   // and zeroes buffers no later stage reads), so that every wait is the same
   // partial count and no branch separates a DMA from the reads after it.
   auto issue_at = [&](int k, bool valid, uint16_t* sa, uint16_t* sb) {
+    const int bk = next_boff(k);
     const int ab = valid ? abytes : 0, bb = valid ? bbytes : 0, so = valid ? k * BKT * 2 : 0;
+    const int sob = valid ? bk : 0;
 #pragma unroll
     for (int j2 = 0; j2 < DPA; ++j2) dma16(A, ab, sa + (wave * DPA + j2) * 512, aoff[j2], so);
 #pragma unroll
-    for (int j2 = 0; j2 < DPB; ++j2) dma16(Bm, bb, sb + (wave * DPB + j2) * 512, boff[j2], so);
+    for (int j2 = 0; j2 < DPB; ++j2) dma16(Bm, bb, sb + (wave * DPB + j2) * 512, boff[j2], sob);
   };
   issue(0, sA0, sB0);
   if constexpr (NST == 4) {
@@ -1052,6 +1121,10 @@ hipError_t launch_pipe(const GemmParams& p, int op, int kind, int split, hipStre
     case EPI_STORE_H16: ST_PIPE_LAUNCH(EPI_STORE_H16, false) break;
     case EPI_RESID_H16: ST_PIPE_LAUNCH(EPI_RESID_H16, false) break;
     case EPI_NCHW: ST_PIPE_LAUNCH(EPI_NCHW, false) break;
+    case EPI_CONV:
+      if (op != ACT_F16) return hipErrorInvalidValue;
+      gemm_pipe_kernel<EPI_CONV, f16_t, WM, WN, FM, FN, MINB, false, NST><<<grid, threads, 0, s>>>(p);
+      break;
     case EPI_HEADS:
       if (ln) { ST_PIPE_LAUNCH(EPI_HEADS, true) } else { ST_PIPE_LAUNCH(EPI_HEADS, false) }
       break;
@@ -1088,6 +1161,16 @@ static int cu_count() {
   return n;
 }
 
+// Convolutions: 128x128 tiles, two per CU (four-stage ring when there are no
+// more tiles than CUs), or 256x256 tiles when there are many of them.
+static hipError_t launch_conv(const GemmParams& p, hipStream_t s) {
+  const long long tiles = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128);
+  const long long big = static_cast<long long>((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big >= kBigTileMin) return launch_pipe<2, 4, 4, 2, 1>(p, ACT_F16, EPI_CONV, 1, s);
+  if (tiles <= cu_count()) return launch_pipe<2, 2, 2, 2, 1, 4>(p, ACT_F16, EPI_CONV, 1, s);
+  return launch_pipe<2, 2, 2, 2, 2>(p, ACT_F16, EPI_CONV, 1, s);
+}
+
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.n_off != 0) return hipErrorInvalidValue;
@@ -1109,6 +1192,15 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
       (!p.epi.out_act || p.N % 64 || p.epi.ldo % 8))
     return hipErrorInvalidValue;
   if (p.K % 64) return hipErrorInvalidValue;
+  if (p.epi.kind == EPI_CONV) {
+    const ConvGemm& cv = p.conv;
+    if (op != ACT_F16 || p.ksplit > 1 || p.epi.ln_stats || !cv.cadd || !cv.out || cv.spt < 1 ||
+        cv.sc_spt < 0 || p.K != (9 * cv.spt + cv.sc_spt) * 64 || cv.Wp % 4 || cv.Wo % 4 ||
+        cv.Wo > cv.Wp || cv.Ho > cv.Hq || p.N % (cv.Hq * cv.Wp) || cv.b_bytes <= 0 ||
+        cv.b_bytes > 0x7fffffffLL || static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL)
+      return hipErrorInvalidValue;
+    return launch_conv(p, s);
+  }
   // the DMA addresses each operand with 32-bit byte offsets
   if (static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL ||
       static_cast<long long>(p.N) * p.ldb * 2 > 0x7fffffffLL)

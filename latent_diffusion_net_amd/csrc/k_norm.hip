@@ -307,6 +307,186 @@ hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int ma
   return hipGetLastError();
 }
 
+// ------------------------------------------- convolution operand (NHWC)
+// GroupNorm apply + SiLU from NCHW into the zero-haloed NHWC operand of a
+// 3x3 convolution: input pixel (i, j) of sample b goes to row (b * (H + 2) +
+// i + 1) * Wp + j + 1 of `out` (L fp16 elements per row, channels from 0);
+// the halo rows and columns are never written (zero from allocation).
+// Optionally the raw input also goes to `raw` (same rows, row length L_raw,
+// channels from raw_cbase): the operand of a fused 1x1 shortcut.  A
+// workgroup owns 64 channels x 64 pixels of one sample, transposed through
+// LDS: 16-byte loads along pixels, 16-byte stores along channels.
+template <typename TI>
+__global__ __launch_bounds__(256) void gn_apply_pad_kernel(
+    const TI* __restrict__ x, const float2* __restrict__ partial, int split,
+    const float* __restrict__ gamma, const float* __restrict__ beta, f16_t* __restrict__ out,
+    int C, int H, int W, int Wp, int L, float eps, f16_t* __restrict__ raw, int L_raw,
+    int raw_cbase, int* __restrict__ range_flag) {
+  __shared__ float2 coef[64];
+  __shared__ float tile[64][64 + 4];  // [channel][pixel], normalised
+  __shared__ float rtile[64][64 + 4];  // raw values (only with `raw`)
+  const int N = H * W;
+  const int n0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int b = blockIdx.z;
+  const int cg = C / kGroups;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int c = c0 + tid;
+    const int g = b * kGroups + c / cg;
+    double s1 = 0.0, s2 = 0.0;
+    for (int i = 0; i < split; ++i) {
+      const float2 pr = partial[g * split + i];
+      s1 += pr.x;
+      s2 += pr.y;
+    }
+    const double n = static_cast<double>(cg) * N;
+    const double shift = to_f32<TI>(x[static_cast<long long>(g) * cg * N]);
+    const double dm = s1 / n;
+    double var = s2 / n - dm * dm;
+    if (var < 0.0) var = 0.0;
+    const float rstd = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
+    const float scale = rstd * gamma[c];
+    coef[tid] = make_float2(scale, beta[c] - static_cast<float>(shift + dm) * scale);
+  }
+  __syncthreads();
+  const bool vec_n = (N & 7) == 0;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = pass * 32 + (tid >> 3);
+    const int nl = 8 * (tid & 7);
+    const int n = n0 + nl;
+    const float2 k = coef[cl];
+    const TI* src = x + (static_cast<long long>(b) * C + c0 + cl) * N + n;
+    float v[8];
+    if (vec_n && n + 7 < N) {
+      load8<TI>(src, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = n + j < N ? to_f32<TI>(src[j]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = fmaf(v[j], k.x, k.y);
+      tile[cl][nl + j] = a / (1.0f + __expf(-a));
+      if (raw) rtile[cl][nl + j] = v[j];
+    }
+  }
+  __syncthreads();
+  bool bad = false;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nl = pass * 32 + (tid >> 3);
+    const int cl = 8 * (tid & 7);
+    const int n = n0 + nl;
+    if (n >= N) continue;
+    const int i = n / W, j = n - (n / W) * W;
+    const long long row = (static_cast<long long>(b) * (H + 2) + i + 1) * Wp + j + 1;
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = tile[cl + q][nl];
+    bad |= store8<f16_t>(out + row * L + c0 + cl, v);
+    if (raw) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = rtile[cl + q][nl];
+      bad |= store8<f16_t>(raw + row * L_raw + raw_cbase + c0 + cl, v);
+    }
+  }
+  if (bad && range_flag) *range_flag = 1;
+}
+
+hipError_t gn_apply_pad(const void* x, const float2* partial, int max_split, const float* gamma,
+                        const float* beta, void* out, int B, int C, int H, int W, int Wp, int L,
+                        float eps, void* raw, int L_raw, int raw_cbase, int* range_flag,
+                        hipStream_t s) {
+  if (C % 64 || L % 8 || L_raw % 8 || raw_cbase % 8) return hipErrorInvalidValue;
+  const int N = H * W;
+  const int split = gn_split(C, N, max_split);
+  dim3 grid((N + 63) / 64, C / 64, B);
+  gn_apply_pad_kernel<bf16_t><<<grid, 256, 0, s>>>(
+      static_cast<const bf16_t*>(x), partial, split, gamma, beta, static_cast<f16_t*>(out), C, H,
+      W, Wp, L, eps, static_cast<f16_t*>(raw), L_raw, raw_cbase, range_flag);
+  return hipGetLastError();
+}
+
+// Time-embedding projection of the ResnetBlock2D, plus the constant terms
+// the first convolution adds: cadd[b][co] = sum_d w[co][d] SiLU(temb[b][d])
+// + temb_b[co] + conv_b[co].  One wavefront per output channel (the weight
+// row read once for every sample), lanes along d, fp32 sums.
+constexpr int kTembMaxB = 16;
+__global__ __launch_bounds__(256) void temb_proj_kernel(
+    const bf16_t* __restrict__ temb, const bf16_t* __restrict__ w,
+    const float* __restrict__ temb_b, const float* __restrict__ conv_b, float* __restrict__ cadd,
+    int B, int Dt, int Cout) {
+  const int co = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (co >= Cout) return;
+  float acc[kTembMaxB];
+#pragma unroll
+  for (int b = 0; b < kTembMaxB; ++b) acc[b] = 0.f;
+  const bf16_t* wr = w + static_cast<long long>(co) * Dt;
+  for (int d = lane; d < Dt; d += 64) {
+    const float wv = bf2f(wr[d]);
+#pragma unroll
+    for (int b = 0; b < kTembMaxB; ++b) {
+      if (b < B) {
+        const float t = bf2f(temb[static_cast<long long>(b) * Dt + d]);
+        acc[b] = fmaf(wv, t / (1.0f + __expf(-t)), acc[b]);
+      }
+    }
+  }
+  const float add = (temb_b ? temb_b[co] : 0.f) + (conv_b ? conv_b[co] : 0.f);
+#pragma unroll
+  for (int b = 0; b < kTembMaxB; ++b) {
+    if (b < B) {
+      const float v = warp_sum(acc[b]);
+      if (lane == 0) cadd[static_cast<long long>(b) * Cout + co] = v + add;
+    }
+  }
+}
+
+hipError_t temb_proj(const void* temb, const void* w, const float* temb_b, const float* conv_b,
+                     float* cadd, int B, int Dt, int Cout, hipStream_t s) {
+  if (B > kTembMaxB) return hipErrorInvalidValue;
+  temb_proj_kernel<<<(Cout + 3) / 4, 256, 0, s>>>(static_cast<const bf16_t*>(temb),
+                                                  static_cast<const bf16_t*>(w), temb_b, conv_b,
+                                                  cadd, B, Dt, Cout);
+  return hipGetLastError();
+}
+int temb_proj_max_batch() { return kTembMaxB; }
+
+// Convolution weights to the GEMM operand: w [Cout][Cin][3][3] (bf16) ->
+// dst [Cout][ldk] fp16 with dst[co][t * Cin + ci] = w[co][ci][t] (tap t = 3
+// di + dj), and, with a 1x1 shortcut, dst[co][9 Cin + ci] = sc[co][ci]
+// (bf16 [Cout][Csc]).  Magnitudes above 65504 set *overflow.
+__global__ void conv_weight_pack_kernel(const bf16_t* __restrict__ w, const bf16_t* __restrict__ sc,
+                                        f16_t* __restrict__ dst, int Cout, int Cin, int Csc,
+                                        int* __restrict__ overflow) {
+  const int ldk = 9 * Cin + Csc;
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long long>(Cout) * ldk) return;
+  const int co = static_cast<int>(idx / ldk);
+  const int k = static_cast<int>(idx - static_cast<long long>(co) * ldk);
+  float v;
+  if (k < 9 * Cin) {
+    const int t = k / Cin, ci = k - (k / Cin) * Cin;
+    v = bf2f(w[(static_cast<long long>(co) * Cin + ci) * 9 + t]);
+  } else {
+    v = bf2f(sc[static_cast<long long>(co) * Csc + (k - 9 * Cin)]);
+  }
+  if (fabsf(v) > 65504.0f) *overflow = 1;
+  dst[idx] = static_cast<f16_t>(v);
+}
+
+hipError_t conv_weight_pack(const void* w, const void* sc, void* dst, int Cout, int Cin, int Csc,
+                            int* overflow, hipStream_t s) {
+  const long long n = static_cast<long long>(Cout) * (9 * Cin + Csc);
+  conv_weight_pack_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(sc), static_cast<f16_t*>(dst), Cout,
+      Cin, Csc, overflow);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------- key padding mask
 __global__ __launch_bounds__(64) void mask_to_bits_kernel(const uint8_t* __restrict__ mask,
                                                           uint32_t* __restrict__ bits, int nk) {

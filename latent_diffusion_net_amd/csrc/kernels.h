@@ -16,7 +16,32 @@ enum EpiKind {
   EPI_NCHW = 4,       // rows = channels, cols = tokens: y = acc + bias[row] + x
   EPI_STORE_H16 = 5,  // out_act (fp16) [row*ldo + col] = fp16(acc + bias[col])
   EPI_RESID_H16 = 6,  // out_act (fp16) [row*ldo + col] = fp16(that value + acc + bias[col])
-  EPI_CROSS_ATTN = 7  // the product is Q of the cross-attention: attend (CrossAttn)
+  EPI_CROSS_ATTN = 7,  // the product is Q of the cross-attention: attend (CrossAttn)
+  EPI_CONV = 8         // implicit-GEMM convolution (ConvGemm): rows = output
+                       // channels, cols = output pixels on the padded grid
+};
+
+// Implicit-GEMM 3x3 convolution (EPI_CONV).  The activations live in a
+// zero-haloed NHWC buffer: pixel row r = (b * Hp + ip) * Wp + jp for the
+// padded position (ip, jp) (input pixel (i, j) at (i + 1, j + 1)), L
+// elements per pixel row.  The product is C[M = Cout][N] = A[Cout][K] (the
+// weights, tap-major: K index t * Cin + ci for tap t = 3 di + dj, then the
+// shortcut's Csc channels) times B^T, where B row m (an output pixel of the
+// padded grid, m = (b * Hq + i) * Wp + j) for tap (di, dj) is buffer row
+// stride * m + di * Wp + dj, channels [0, Cin); the shortcut segment reads
+// buffer row stride * m + sc_roff, channels [sc_cbase, sc_cbase + Csc).
+// GEMM parameters: B = the buffer, ldb = stride * L, N = B * Hq * Wp; the
+// K stages (64 deep) walk the taps in order, spt = Cin / 64 stages per tap,
+// sc_spt = Csc / 64 after them.  Output pixel m is valid when i < Ho and
+// j < Wo; its value acc + cadd[b * M + row] (+ resid, NCHW, when given)
+// is stored to out NCHW [B][M][Ho][Wo] as bf16.
+struct ConvGemm {
+  int L, Wp, Hq, Ho, Wo;
+  int spt, sc_spt, sc_cbase, sc_roff;
+  long long b_bytes;        // bytes of the activation buffer (reads past it return 0)
+  const float* cadd;        // [B][M] per sample and output channel (bias + time embedding)
+  const void* resid;        // NCHW [B][M][Ho][Wo] bf16, or NULL
+  void* out;                // NCHW [B][M][Ho][Wo] bf16
 };
 
 // Cross-attention in the epilogue of its Q projection (EPI_CROSS_ATTN).
@@ -108,6 +133,7 @@ struct GemmParams {
   // First output column this launch computes (set by gemm_mfma when it
   // splits a product's columns between two tile shapes; callers leave 0).
   int n_off;
+  ConvGemm conv;  // EPI_CONV only
 };
 
 // MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
@@ -173,6 +199,24 @@ hipError_t gn_apply_tokens(const void* x, bool bf16, const float2* partial,
 hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int max_split,
                          const void* gamma, const void* beta, void* y, int B, int C, int N,
                          float eps, bool silu, hipStream_t s);
+// ResnetBlock2D helpers.  gn_apply_pad: GroupNorm apply + SiLU of NCHW
+// bf16 x (partials of gn_stats) into the zero-haloed NHWC fp16 operand of a
+// 3x3 convolution (row (b (H + 2) + i + 1) Wp + j + 1, L elements per row);
+// with `raw`, the raw x also to raw (row length L_raw, channels from
+// raw_cbase).  C % 64 == 0.  gamma, beta fp32.
+hipError_t gn_apply_pad(const void* x, const float2* partial, int max_split, const float* gamma,
+                        const float* beta, void* out, int B, int C, int H, int W, int Wp, int L,
+                        float eps, void* raw, int L_raw, int raw_cbase, int* range_flag,
+                        hipStream_t s);
+// cadd[b][co] = w[co] . SiLU(temb[b]) + temb_b[co] + conv_b[co] (bf16 temb
+// and w, fp32 biases, NULL = 0); B <= temb_proj_max_batch().
+hipError_t temb_proj(const void* temb, const void* w, const float* temb_b, const float* conv_b,
+                     float* cadd, int B, int Dt, int Cout, hipStream_t s);
+int temb_proj_max_batch();
+// 3x3 convolution weights [Cout][Cin][3][3] bf16 (+ 1x1 shortcut [Cout][Csc])
+// -> tap-major fp16 GEMM operand [Cout][9 Cin + Csc].
+hipError_t conv_weight_pack(const void* w, const void* sc, void* dst, int Cout, int Cin, int Csc,
+                            int* overflow, hipStream_t s);
 // Key padding mask [B][nk] bytes (nonzero = attend) -> bits [B][4] words
 // (bit k of word w: key 32 w + k; keys >= nk clear); nk <= 96.
 hipError_t mask_to_bits(const uint8_t* mask, uint32_t* bits, int B, int nk, hipStream_t s);

@@ -189,3 +189,59 @@ def small_config(name: str = "small", *, B=2, C=128, H=15, W=15, heads=None,
     """A parity-test configuration the oracle finishes in well under a second."""
     return BlockConfig(name, B, C, H, W, heads if heads is not None else C // 64,
                        D_ctx, depth, dtype)
+
+
+# ------------------------------------------------------------ ResnetBlock2D
+@dataclasses.dataclass(frozen=True)
+class ResnetConfig:
+    """Shape of one ResnetBlock2D invocation (x [B, Cin, H, W], temb [B, Dt])."""
+    name: str
+    B: int
+    Cin: int
+    Cout: int
+    H: int
+    W: int
+    Dt: int = 1280  # time-embedding width of the SD / SDXL U-Nets (4 x 320)
+
+
+RESNET_WEIGHTS = ("conv1_w", "temb_w", "conv2_w", "sc_w")
+
+
+def make_resnet_inputs(cfg: ResnetConfig, seed: int, *, weight_std: float = 0.02,
+                       bias_std: float = 0.0, norm_std: float = 0.0) -> Dict:
+    """Draw x, temb and every ResnetBlock2D parameter, rounded to bf16.
+
+    Draw order with ``numpy.random.default_rng(seed)``: x, temb, conv1_w,
+    temb_w, conv2_w, then sc_w when Cin != Cout; weights N(0, weight_std^2),
+    x and temb N(0, 1).  Stress draws (biases, GroupNorm gammas/betas) come
+    from a second generator seeded ``seed + 7919``; by default biases are 0,
+    gammas 1, betas 0.
+    """
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    B, Ci, Co, H, W, Dt = cfg.B, cfg.Cin, cfg.Cout, cfg.H, cfg.W, cfg.Dt
+
+    def normal(shape, std):
+        return (rng.standard_normal(size=shape, dtype=f32) * f32(std)).astype(f32)
+
+    x = normal((B, Ci, H, W), 1.0)
+    temb = normal((B, Dt), 1.0)
+    p = {"conv1_w": normal((Co, Ci, 3, 3), weight_std), "temb_w": normal((Co, Dt), weight_std),
+         "conv2_w": normal((Co, Co, 3, 3), weight_std)}
+    if Ci != Co:
+        p["sc_w"] = normal((Co, Ci), weight_std)
+    rng2 = np.random.default_rng(seed + 7919)
+
+    def extra(n, mean, std):
+        if std > 0:
+            return (mean + rng2.standard_normal(size=n, dtype=f32) * f32(std)).astype(f32)
+        return np.full(n, mean, f32)
+
+    p["gn1_w"], p["gn1_b"] = extra(Ci, 1.0, norm_std), extra(Ci, 0.0, norm_std)
+    p["conv1_b"], p["temb_b"] = extra(Co, 0.0, bias_std), extra(Co, 0.0, bias_std)
+    p["gn2_w"], p["gn2_b"] = extra(Co, 1.0, norm_std), extra(Co, 0.0, norm_std)
+    p["conv2_b"] = extra(Co, 0.0, bias_std)
+    if Ci != Co:
+        p["sc_b"] = extra(Co, 0.0, bias_std)
+    return {"x": round_bf16(x), "temb": round_bf16(temb),
+            "params": {k: round_bf16(v) for k, v in p.items()}}

@@ -229,3 +229,33 @@ def test_ops_validate_before_any_device_call():
                dict(dt=3), dict(eps=None), dict(s=float("inf"))]:
         assert dd(**kw) == binding.ST_ERR_INVALID, kw
     assert dd(n=0, eps=None, xt=None, xp=None) == binding.ST_OK  # nothing to do
+
+
+def test_resnet_create_validates_before_any_device_call():
+    lib = _lib()
+    P = 0x10000
+    w = binding.ResnetWeights()
+    w.conv1_w = w.conv2_w = w.temb_w = w.sc_w = P
+
+    def create(B=2, Ci=64, Co=64, H=8, W=8, Dt=32, eps=1e-5, dt=0, ww=w):
+        h = ctypes.c_void_p()
+        st = lib.st_resnet_create(B, Ci, Co, H, W, Dt, eps, dt,
+                                  ctypes.byref(ww) if ww is not None else None, None, ctypes.byref(h))
+        assert h.value is None
+        return st
+    assert create(B=0) == binding.ST_ERR_INVALID
+    assert create(Ci=96) == binding.ST_ERR_INVALID
+    assert create(Co=0) == binding.ST_ERR_INVALID
+    assert create(eps=0.0) == binding.ST_ERR_INVALID
+    assert create(dt=4) == binding.ST_ERR_INVALID
+    assert create(dt=1) == binding.ST_ERR_UNSUPPORTED      # fp32 storage
+    assert create(B=17) == binding.ST_ERR_UNSUPPORTED      # time-embedding batch limit
+    assert create(W=6) == binding.ST_ERR_UNSUPPORTED       # width not a multiple of 4
+    assert create(ww=None) == binding.ST_ERR_INVALID
+    nosc = binding.ResnetWeights()
+    nosc.conv1_w = nosc.conv2_w = nosc.temb_w = P
+    assert create(Co=128, ww=nosc) == binding.ST_ERR_INVALID  # projection needs sc_w
+    assert create(H=4096, W=4096, Ci=640, Co=640) == binding.ST_ERR_UNSUPPORTED
+    assert lib.st_resnet_forward(None, P, P, P, None) == binding.ST_ERR_INVALID
+    assert lib.st_resnet_check_range(None, None) == binding.ST_ERR_INVALID
+    lib.st_resnet_destroy(None)
