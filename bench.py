@@ -220,6 +220,90 @@ def cpu_baseline(cfg, inp):
             "sample": f"one full fp64 forward of the same workload ({cfg.T} tokens), {dt:.1f} s"}
 
 
+def _event_times(torch, fn, reps, stream):
+    """Per-call milliseconds of ``fn`` (one HIP event pair each, on ``stream``)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _rate(ms_list, work, unit, peak):
+    med = statistics.median(ms_list)
+    a = work / (med * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"us_median": round(med * 1e3, 2), "us_min": round(min(ms_list) * 1e3, 2),
+            "achieved": round(a, 1), "unit": unit, "peak": peak, "frac": round(a / peak, 3)}
+
+
+def resnet_flops(cfg) -> float:
+    """Both 3x3 convolutions (and a 1x1 shortcut) of one ResnetBlock2D."""
+    n = cfg.B * cfg.H * cfg.W
+    f = 2.0 * n * cfg.Cout * 9 * cfg.Cin + 2.0 * n * cfg.Cout * 9 * cfg.Cout
+    if cfg.Cin != cfg.Cout:
+        f += 2.0 * n * cfg.Cout * cfg.Cin
+    return f
+
+
+def next_rows(torch, cfg_block, blk_inputs, stream, reps=20):
+    """Measured rates of the parts built around the block: a ResnetBlock2D at
+    the bench stage, the GroupNorm(+SiLU) op, the guided DDPM step and the
+    block forward with a context key padding mask."""
+    from latent_diffusion_net_amd import STResnet, synth
+    from latent_diffusion_net_amd.binding import group_norm, guided_ddpm_step
+    out = {}
+    dev = "cuda:0"
+    # ResnetBlock2D at the SDXL Down1 stage (640 channels, 64 x 64, B = 2)
+    rc = synth.ResnetConfig("sdxl_down1_640_64x64", 2, 640, 640, 64, 64)
+    ri = synth.make_resnet_inputs(rc, 1)
+    bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
+    rp = {k: bf(v) for k, v in ri["params"].items()}
+    rx, rt = bf(ri["x"]), bf(ri["temb"])
+    ry = torch.empty_like(rx)
+    res = STResnet(rc.B, rc.Cin, rc.Cout, rc.H, rc.W, rc.Dt, rp)
+    for _ in range(3):
+        res.forward(rx, rt, ry, stream)
+    ms = _event_times(torch, lambda: res.forward(rx, rt, ry, stream), reps, stream)
+    res.close()
+    out["F1 ResnetBlock2D (SDXL Down1, 640 ch, 64x64, B=2)"] = dict(
+        _rate(ms, resnet_flops(rc), "TFLOP/s", BF16_PEAK_TFLOPS), flops=resnet_flops(rc),
+        bound="mfma (the two 3x3 convolutions; GroupNorm passes and the time embedding inside)")
+    # GroupNorm + SiLU op on the same map: read once, write once at least
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    gy = torch.empty_like(rx)
+    group_norm(rx, None, None, 1e-5, True, gy, ws, stream)
+    ms = _event_times(torch, lambda: group_norm(rx, None, None, 1e-5, True, gy, ws, stream), reps, stream)
+    out["GroupNorm + SiLU op (2 x 640 x 64 x 64 bf16)"] = dict(
+        _rate(ms, 2.0 * rx.numel() * 2, "GB/s", HBM_PEAK_GBS), bytes=2.0 * rx.numel() * 2,
+        bound="hbm (algorithmic: x read once, y written once; the kernels read x twice)")
+    # guided DDPM step on an SDXL latent (4 x 128 x 128)
+    n = 4 * 128 * 128
+    eps = torch.randn(2, n, device=dev).to(torch.bfloat16)
+    xt = torch.randn(n, device=dev)
+    z = torch.randn(n, device=dev)
+    xp = torch.empty_like(xt)
+    guided_ddpm_step(eps, xt, 500, 7.5, z, xp, stream=stream)
+    ms = _event_times(torch, lambda: guided_ddpm_step(eps, xt, 500, 7.5, z, xp, stream=stream), reps, stream)
+    out["F4 guidance + DDPM step (4 x 128 x 128 latent)"] = dict(
+        _rate(ms, 2.0 * 2 * n + 4.0 * 3 * n, "GB/s", HBM_PEAK_GBS), bytes=2.0 * 2 * n + 4.0 * 3 * n,
+        bound="hbm (a 1 MB step: launch latency dominates)")
+    # block forward with a padded context mask (the first 20 tokens real)
+    blk, x, ctx, y = blk_inputs
+    m = torch.zeros((cfg_block.B, 77), dtype=torch.uint8, device=dev)
+    m[:, :20] = 1
+    blk.forward_masked(x, ctx, m, y, stream)
+    ms = _event_times(torch, lambda: blk.forward_masked(x, ctx, m, y, stream), reps, stream)
+    ms0 = _event_times(torch, lambda: blk.forward(x, ctx, y, stream), reps, stream)
+    out["F3 block forward with a context key mask (bench workload)"] = {
+        "us_median": round(statistics.median(ms) * 1e3, 2),
+        "us_median_unmasked_same_run": round(statistics.median(ms0) * 1e3, 2),
+        "tokens_per_s": cfg_block.T / (statistics.median(ms) * 1e-3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +312,8 @@ def main():
     ap.add_argument("--config", type=int, default=DEFAULT_WORKLOAD,
                     help="workload index (default: the SDXL Down1 block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the ResnetBlock2D / GroupNorm / DDPM / masked-forward measurements")
     ap.add_argument("--kernels", action="store_true",
                     help="also print the per-step microseconds of every kernel kind")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -312,6 +398,7 @@ def main():
     kt = blk.read_timing()
     blk.set_timing([])
     kernels = {k: round(v["ms"] / 5 * 1e3, 2) for k, v in kt.items()} if args.kernels else None
+    nxt = None if args.no_next_rows else next_rows(torch, cfg, (blk, x, ctx, y), stream)
     blk.close()
     copy_gbs = copy_ceiling_gbs(torch, dev)
     rows = row_rates(cfg, kt, copy_gbs)
@@ -359,6 +446,8 @@ def main():
     }
     if kernels is not None:
         result["kernel_us_per_step"] = kernels
+    if nxt is not None:
+        result["next_rows"] = nxt
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)

@@ -55,7 +55,8 @@ typedef struct {
 /*
  * Create a ResnetBlock2D handle on the current HIP device.
  *   1 <= B <= 16; Cin, Cout positive multiples of 64; H >= 1; W >= 4 and
- *   W % 4 == 0 (other widths: ST_ERR_UNSUPPORTED); Dt >= 1; eps > 0;
+ *   W % 4 == 0 (other widths: ST_ERR_UNSUPPORTED); Dt >= 1, with Dt % 8 ==
+ *   0 and B * Dt <= 16384 (else ST_ERR_UNSUPPORTED); eps > 0;
  *   dtype ST_DTYPE_BF16 (ST_DTYPE_F32: ST_ERR_UNSUPPORTED).
  *   w: device pointers as above, weights non-NULL and 16-byte aligned.  The
  *      weights are COPIED and repacked (tap-major fp16 convolution operands;

@@ -411,13 +411,22 @@ hipError_t gn_apply_pad(const void* x, const float2* partial, int max_split, con
 
 // Time-embedding projection of the ResnetBlock2D, plus the constant terms
 // the first convolution adds: cadd[b][co] = sum_d w[co][d] SiLU(temb[b][d])
-// + temb_b[co] + conv_b[co].  One wavefront per output channel (the weight
-// row read once for every sample), lanes along d, fp32 sums.
+// + temb_b[co] + conv_b[co].  SiLU(temb) of every sample is computed once
+// per workgroup into LDS; then one wavefront per output channel, each lane
+// taking eight consecutive d of the weight row (one 16-byte load), fp32
+// sums reduced across the wavefront.
 constexpr int kTembMaxB = 16;
+constexpr int kTembMaxFloats = 16384;  // B * Dt floats of SiLU(temb) held in LDS (64 KB)
 __global__ __launch_bounds__(256) void temb_proj_kernel(
     const bf16_t* __restrict__ temb, const bf16_t* __restrict__ w,
     const float* __restrict__ temb_b, const float* __restrict__ conv_b, float* __restrict__ cadd,
     int B, int Dt, int Cout) {
+  extern __shared__ float st[];  // [B][Dt]
+  for (int i = threadIdx.x; i < B * Dt; i += 256) {
+    const float t = bf2f(temb[i]);
+    st[i] = t / (1.0f + __expf(-t));
+  }
+  __syncthreads();
   const int co = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (co >= Cout) return;
@@ -425,13 +434,15 @@ __global__ __launch_bounds__(256) void temb_proj_kernel(
 #pragma unroll
   for (int b = 0; b < kTembMaxB; ++b) acc[b] = 0.f;
   const bf16_t* wr = w + static_cast<long long>(co) * Dt;
-  for (int d = lane; d < Dt; d += 64) {
-    const float wv = bf2f(wr[d]);
+  for (int d0 = lane * 8; d0 < Dt; d0 += 512) {
+    float wv[8];
+    load8<bf16_t>(wr + d0, wv);
 #pragma unroll
     for (int b = 0; b < kTembMaxB; ++b) {
       if (b < B) {
-        const float t = bf2f(temb[static_cast<long long>(b) * Dt + d]);
-        acc[b] = fmaf(wv, t / (1.0f + __expf(-t)), acc[b]);
+        const float* sb = st + b * Dt + d0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[b] = fmaf(wv[q], sb[q], acc[b]);
       }
     }
   }
@@ -447,13 +458,16 @@ __global__ __launch_bounds__(256) void temb_proj_kernel(
 
 hipError_t temb_proj(const void* temb, const void* w, const float* temb_b, const float* conv_b,
                      float* cadd, int B, int Dt, int Cout, hipStream_t s) {
-  if (B > kTembMaxB) return hipErrorInvalidValue;
-  temb_proj_kernel<<<(Cout + 3) / 4, 256, 0, s>>>(static_cast<const bf16_t*>(temb),
-                                                  static_cast<const bf16_t*>(w), temb_b, conv_b,
-                                                  cadd, B, Dt, Cout);
+  // rows of 8-element (16-byte) loads; SiLU(temb) of all samples in LDS
+  if (!temb_proj_supported(B, Dt)) return hipErrorInvalidValue;
+  temb_proj_kernel<<<(Cout + 3) / 4, 256, sizeof(float) * B * Dt, s>>>(
+      static_cast<const bf16_t*>(temb), static_cast<const bf16_t*>(w), temb_b, conv_b, cadd, B, Dt,
+      Cout);
   return hipGetLastError();
 }
-int temb_proj_max_batch() { return kTembMaxB; }
+bool temb_proj_supported(int B, int Dt) {
+  return B >= 1 && B <= kTembMaxB && Dt >= 8 && Dt % 8 == 0 && B * Dt <= kTembMaxFloats;
+}
 
 // Convolution weights to the GEMM operand: w [Cout][Cin][3][3] (bf16) ->
 // dst [Cout][ldk] fp16 with dst[co][t * Cin + ci] = w[co][ci][t] (tap t = 3

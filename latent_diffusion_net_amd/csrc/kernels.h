@@ -209,10 +209,11 @@ hipError_t gn_apply_pad(const void* x, const float2* partial, int max_split, con
                         float eps, void* raw, int L_raw, int raw_cbase, int* range_flag,
                         hipStream_t s);
 // cadd[b][co] = w[co] . SiLU(temb[b]) + temb_b[co] + conv_b[co] (bf16 temb
-// and w, fp32 biases, NULL = 0); B <= temb_proj_max_batch().
+// and w, fp32 biases, NULL = 0); needs temb_proj_supported(B, Dt): B <= 16,
+// Dt % 8 == 0 and B * Dt <= 16384.
 hipError_t temb_proj(const void* temb, const void* w, const float* temb_b, const float* conv_b,
                      float* cadd, int B, int Dt, int Cout, hipStream_t s);
-int temb_proj_max_batch();
+bool temb_proj_supported(int B, int Dt);
 // 3x3 convolution weights [Cout][Cin][3][3] bf16 (+ 1x1 shortcut [Cout][Csc])
 // -> tap-major fp16 GEMM operand [Cout][9 Cin + Csc].
 hipError_t conv_weight_pack(const void* w, const void* sc, void* dst, int Cout, int Cin, int Csc,

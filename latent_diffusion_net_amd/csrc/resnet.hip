@@ -148,7 +148,9 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
   if (!(eps > 0.f) || !std::isfinite(eps)) return fail(ST_ERR_INVALID, "eps must be positive");
   if (dtype != ST_DTYPE_BF16 && dtype != ST_DTYPE_F32) return fail(ST_ERR_INVALID, "unknown dtype");
   if (dtype != ST_DTYPE_BF16) return fail(ST_ERR_UNSUPPORTED, "the ResnetBlock2D runs with bf16 storage only");
-  if (B > temb_proj_max_batch()) return fail(ST_ERR_UNSUPPORTED, "B must be <= 16");
+  if (B > 16) return fail(ST_ERR_UNSUPPORTED, "B must be <= 16");
+  if (!temb_proj_supported(B, Dt))
+    return fail(ST_ERR_UNSUPPORTED, "the time embedding needs Dt % 8 == 0 and B * Dt <= 16384");
   if (W % 4) return fail(ST_ERR_UNSUPPORTED, "W must be a multiple of 4");
   if (!w) return fail(ST_ERR_INVALID, "weights are NULL");
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };

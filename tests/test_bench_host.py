@@ -146,3 +146,12 @@ def test_row_work_rates_context_kv_on_hbm_and_counts_fused_cross_attention(bench
 
 def test_cpu_model_is_reported(bench):
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_resnet_flops(bench):
+    from latent_diffusion_net_amd import synth
+    c = synth.ResnetConfig("r", 2, 320, 640, 64, 64)
+    n = 2 * 64 * 64
+    assert bench.resnet_flops(c) == 2.0 * n * 640 * 9 * 320 + 2.0 * n * 640 * 9 * 640 + 2.0 * n * 640 * 320
+    c = synth.ResnetConfig("r", 2, 640, 640, 64, 64)
+    assert bench.resnet_flops(c) == pytest.approx(120.8e9, rel=1e-3)
