@@ -245,3 +245,169 @@ def make_resnet_inputs(cfg: ResnetConfig, seed: int, *, weight_std: float = 0.02
         p["sc_b"] = extra(Co, 0.0, bias_std)
     return {"x": round_bf16(x), "temb": round_bf16(temb),
             "params": {k: round_bf16(v) for k, v in p.items()}}
+
+
+# ------------------------------------------------------------------ U-Net
+@dataclasses.dataclass(frozen=True)
+class UNetConfig:
+    """Topology of a U-Net denoiser (the pages' §3 diagrams).
+
+    ``channels`` and ``depths`` per resolution level (depth 0 = ResNet only,
+    no Spatial-Transformer), ``mid_depth`` for the middle block,
+    ``layers_per_block`` ResNets per down level (up levels take one more),
+    ``ctx_dim`` the context width, ``add_in`` the width of an extra
+    embedding added to the time embedding (SDXL: pooled text + size and crop
+    conditions, 2816), 0 = none.  The time embedding is sinusoidal of width
+    channels[0], then Linear -> SiLU -> Linear to 4 channels[0].
+    """
+    name: str
+    in_channels: int
+    out_channels: int
+    channels: tuple
+    depths: tuple
+    mid_depth: int
+    layers_per_block: int
+    ctx_dim: int
+    add_in: int = 0
+
+    @property
+    def temb_in(self) -> int:
+        return self.channels[0]
+
+    @property
+    def temb_dim(self) -> int:
+        return 4 * self.channels[0]
+
+
+UNET_CONFIGS = {
+    # SD2.1-base architecture page §3: Down 0-2 with cross-attention, Down 3
+    # and Up 0 ResNet only, 4 -> 4 channels, context [1, 77, 1024]
+    "sd21": UNetConfig("sd21_base", 4, 4, (320, 640, 1280, 1280), (1, 1, 1, 0), 1, 2, 1024),
+    # SDXL-Inpaint architecture page §3: Down 0 ResNet only, Down 1 / Down 2
+    # with cross-attention (depth 2 and 10, tutorial), 9 -> 4 channels,
+    # context [1, 77, 2048]; the time embedding also takes the pooled text
+    # and size/crop conditions (tutorial)
+    "sdxl_inpaint": UNetConfig("sdxl_inpaint", 9, 4, (320, 640, 1280), (0, 2, 10), 10, 2, 2048, 2816),
+}
+
+
+def unet_skip_channels(cfg: UNetConfig) -> List[int]:
+    """Channels of the skip connections in the order the down path stores
+    them: conv_in's output, every down-level ResNet (+ transformer) output,
+    every downsampler's output."""
+    sk = [cfg.channels[0]]
+    for lvl, c in enumerate(cfg.channels):
+        sk += [c] * cfg.layers_per_block
+        if lvl < len(cfg.channels) - 1:
+            sk.append(c)
+    return sk
+
+
+def unet_param_shapes(cfg: UNetConfig) -> Dict:
+    """Nested dict of parameter shapes (no values): the module structure of
+    the U-Net, in the order the draws are taken."""
+    C0, Td = cfg.channels[0], cfg.temb_dim
+    P = {"time1_w": (Td, cfg.temb_in), "time1_b": (Td,), "time2_w": (Td, Td), "time2_b": (Td,)}
+    if cfg.add_in:
+        P.update({"add1_w": (Td, cfg.add_in), "add1_b": (Td,), "add2_w": (Td, Td), "add2_b": (Td,)})
+    P["conv_in_w"] = (C0, cfg.in_channels, 3, 3)
+    P["conv_in_b"] = (C0,)
+
+    def resnet(ci, co):
+        r = {"gn1_w": (ci,), "gn1_b": (ci,), "conv1_w": (co, ci, 3, 3), "conv1_b": (co,),
+             "temb_w": (co, Td), "temb_b": (co,), "gn2_w": (co,), "gn2_b": (co,),
+             "conv2_w": (co, co, 3, 3), "conv2_b": (co,)}
+        if ci != co:
+            r["sc_w"] = (co, ci)
+            r["sc_b"] = (co,)
+        return r
+
+    def block(c, depth):
+        D, F = cfg.ctx_dim, 4 * c
+        lay = {"ln1_w": (c,), "ln1_b": (c,), "q1_w": (c, c), "k1_w": (c, c), "v1_w": (c, c),
+               "o1_w": (c, c), "o1_b": (c,), "ln2_w": (c,), "ln2_b": (c,), "q2_w": (c, c),
+               "k2_w": (c, D), "v2_w": (c, D), "o2_w": (c, c), "o2_b": (c,), "ln3_w": (c,),
+               "ln3_b": (c,), "ff1_w": (2 * F, c), "ff1_b": (2 * F,), "ff2_w": (c, F),
+               "ff2_b": (c,)}
+        return {"gn_w": (c,), "gn_b": (c,), "proj_in_w": (c, c), "proj_in_b": (c,),
+                "proj_out_w": (c, c), "proj_out_b": (c,), "layers": [dict(lay) for _ in range(depth)]}
+
+    down, h = [], C0
+    for lvl, c in enumerate(cfg.channels):
+        d = {"res": [], "attn": []}
+        for _ in range(cfg.layers_per_block):
+            d["res"].append(resnet(h, c))
+            h = c
+            if cfg.depths[lvl]:
+                d["attn"].append(block(c, cfg.depths[lvl]))
+        if lvl < len(cfg.channels) - 1:
+            d["down_w"], d["down_b"] = (c, c, 3, 3), (c,)
+        down.append(d)
+    P["down"] = down
+    P["mid"] = {"res": [resnet(h, h), resnet(h, h)],
+                "attn": [block(h, cfg.mid_depth)] if cfg.mid_depth else []}
+    skips = unet_skip_channels(cfg)
+    up = []
+    for lvl in reversed(range(len(cfg.channels))):
+        c = cfg.channels[lvl]
+        u = {"res": [], "attn": []}
+        for _ in range(cfg.layers_per_block + 1):
+            u["res"].append(resnet(h + skips.pop(), c))
+            h = c
+            if cfg.depths[lvl]:
+                u["attn"].append(block(c, cfg.depths[lvl]))
+        if lvl > 0:
+            u["up_w"], u["up_b"] = (c, c, 3, 3), (c,)
+        up.append(u)
+    P["up"] = up
+    P["norm_out_w"], P["norm_out_b"] = (C0,), (C0,)
+    P["conv_out_w"], P["conv_out_b"] = (cfg.out_channels, C0, 3, 3), (cfg.out_channels,)
+    return P
+
+
+def _walk(tree, fn, path=()):
+    """Map ``fn(path, leaf)`` over a nested dict / list tree, in key order
+    as written (dicts keep insertion order)."""
+    if isinstance(tree, dict):
+        return {k: _walk(v, fn, path + (k,)) for k, v in tree.items()}
+    if isinstance(tree, list):
+        return [_walk(v, fn, path + (i,)) for i, v in enumerate(tree)]
+    return fn(path, tree)
+
+
+def unet_param_count(cfg: UNetConfig) -> int:
+    n = [0]
+
+    def f(path, shape):
+        n[0] += int(np.prod(shape))
+        return shape
+    _walk(unet_param_shapes(cfg), f)
+    return n[0]
+
+
+def make_unet_inputs(cfg: UNetConfig, seed: int, B: int, H: int, W: int, *,
+                     weight_std: float = 0.02, t=(999.0,)) -> Dict:
+    """Draw x [B, in, H, W], ctx [B, 77, D], add [B, add_in] (N(0, 1)), the
+    timesteps (``t`` repeated to B values) and every U-Net parameter: weights
+    (names ending in ``_w`` except norm gammas) N(0, weight_std^2) in
+    ``unet_param_shapes`` order, biases 0, norm gammas 1, betas 0.  All
+    rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    x = rng.standard_normal((B, cfg.in_channels, H, W), dtype=f32)
+    ctx = rng.standard_normal((B, CTX_LEN, cfg.ctx_dim), dtype=f32)
+    add = rng.standard_normal((B, cfg.add_in), dtype=f32) if cfg.add_in else None
+    norm_w = ("gn1_w", "gn2_w", "gn_w", "norm_out_w", "ln1_w", "ln2_w", "ln3_w")
+
+    def draw(path, shape):
+        name = path[-1]
+        if name in norm_w:
+            return np.ones(shape, f32)
+        if name.endswith("_w"):
+            return round_bf16((rng.standard_normal(size=shape, dtype=f32) * f32(weight_std)).astype(f32))
+        return np.zeros(shape, f32)
+
+    params = _walk(unet_param_shapes(cfg), draw)
+    tt = np.array([t[i % len(t)] for i in range(B)], np.float32)
+    return {"x": round_bf16(x), "ctx": round_bf16(ctx),
+            "add": round_bf16(add) if add is not None else None, "t": tt, "params": params}

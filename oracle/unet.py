@@ -162,3 +162,81 @@ def guided_ddpm_step(x_t, eps_pair, t: int, scale: float, schedule, noise=None):
     eps_pair = _f64(eps_pair)
     n = eps_pair.shape[0] // 2
     return ddpm_step(x_t, cfg_combine(eps_pair[:n], eps_pair[n:], scale), t, schedule, noise)
+
+
+# ------------------------------------------------------------------ U-Net
+def timestep_embedding(t, dim: int):
+    """Sinusoidal embedding of the timesteps t [B] -> [B, dim] (the
+    tutorial's sinusoidal embedding).  Reading taken: half = dim / 2
+    frequencies f_i = 10000^(-i / half), i = 0 .. half - 1, and the cosines
+    first: [cos(t f_0) .. cos(t f_{half-1}), sin(t f_0) .. sin(t f_{half-1})]."""
+    t = _f64(t).reshape(-1)
+    half = dim // 2
+    f = np.exp(-math.log(10000.0) * np.arange(half, dtype=np.float64) / half)
+    a = t[:, None] * f[None, :]
+    return np.concatenate([np.cos(a), np.sin(a)], axis=1)
+
+
+def unet_forward(x, t, ctx, P: Dict, cfg, add=None, record=None):
+    """One denoiser timestep of the U-Net, x [B, in, H, W] -> [B, out, H, W].
+
+    Follows the architecture pages' §3 topology (SDXL-Inpaint, SD2.1): the
+    time embedding (sinusoidal, Linear -> SiLU -> Linear, plus the same MLP
+    on ``add`` when the configuration has one); conv_in; per down level
+    ``layers_per_block`` x (ResnetBlock2D, then a Spatial-Transformer block
+    of the level's depth when it has one), each output kept as a skip, then
+    a 3x3 stride-2 convolution (DownSample, tutorial) except on the last
+    level, its output kept as a skip too; the middle block ResNet ->
+    transformer -> ResNet; per up level, deepest first, (layers_per_block +
+    1) x (concatenate the last kept skip along channels, ResnetBlock2D,
+    transformer), then nearest 2x upsampling and a 3x3 convolution
+    (UpSample, tutorial) except on the last; GroupNorm + SiLU + 3x3 conv_out.
+    GroupNorms of the ResNets and of the output use eps 1e-5; the
+    transformer blocks are oracle.block.block_forward (heads = C / 64).
+    ``record`` (a list) receives (stage name, shape) of every stage output.
+    """
+    from .block import block_forward
+    x = _f64(x)
+    emb = timestep_embedding(t, cfg.temb_in)
+    temb = linear(silu(linear(emb, P["time1_w"], P["time1_b"])), P["time2_w"], P["time2_b"])
+    if cfg.add_in:
+        temb = temb + linear(silu(linear(add, P["add1_w"], P["add1_b"])), P["add2_w"], P["add2_b"])
+
+    def rec(name, a):
+        if record is not None:
+            record.append((name, tuple(a.shape)))
+        return a
+
+    def st(h, bp):
+        return block_forward(h, ctx, bp, h.shape[1] // 64)
+
+    h = rec("conv_in", conv2d(x, P["conv_in_w"], P["conv_in_b"]))
+    skips = [h]
+    L = len(cfg.channels)
+    for lvl in range(L):
+        d = P["down"][lvl]
+        for r in range(cfg.layers_per_block):
+            h = resnet_block(h, temb, d["res"][r])
+            if cfg.depths[lvl]:
+                h = st(h, d["attn"][r])
+            skips.append(rec(f"down{lvl}.{r}", h))
+        if lvl < L - 1:
+            h = conv2d(h, d["down_w"], d["down_b"], stride=2)
+            skips.append(rec(f"down{lvl}.downsample", h))
+    m = P["mid"]
+    h = resnet_block(h, temb, m["res"][0])
+    if cfg.mid_depth:
+        h = st(h, m["attn"][0])
+    h = rec("mid", resnet_block(h, temb, m["res"][1]))
+    for u, lvl in enumerate(reversed(range(L))):
+        up = P["up"][u]
+        for r in range(cfg.layers_per_block + 1):
+            h = np.concatenate([h, skips.pop()], axis=1)
+            h = resnet_block(h, temb, up["res"][r])
+            if cfg.depths[lvl]:
+                h = st(h, up["attn"][r])
+        rec(f"up{u}", h)
+        if lvl > 0:
+            h = rec(f"up{u}.upsample", conv2d(upsample_nearest2x(h), up["up_w"], up["up_b"]))
+    h = silu(group_norm(h, P["norm_out_w"], P["norm_out_b"], 32, 1e-5))
+    return rec("conv_out", conv2d(h, P["conv_out_w"], P["conv_out_b"]))

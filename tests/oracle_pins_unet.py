@@ -302,4 +302,78 @@ def pin_mask_brute_whole_block():
     _close(y, np.array(yb), 1e-11, "masked block vs brute force")
 
 
+
+# ------------------------------------------------------------------ U-Net
+def _golden(name):
+    return [l.split() for l in open(os.path.join(GOLDEN, name))
+            if l.strip() and not l.startswith("#")]
+
+
+def pin_unet_parameter_counts_from_the_pages():
+    """The U-Net structure reproduces the parameter counts the pages print:
+    SD1.5 (the SD2.1 topology with a 768-wide context) about 860M, SDXL
+    Base (4 input channels) 5.14G in FP16 = 2.57e9."""
+    import dataclasses
+    cfgs = {"sd15": dataclasses.replace(synth.UNET_CONFIGS["sd21"], ctx_dim=768),
+            "sdxl_base": dataclasses.replace(synth.UNET_CONFIGS["sdxl_inpaint"], in_channels=4)}
+    for name, n, tol in _golden("unet_params.txt"):
+        got = synth.unet_param_count(cfgs[name])
+        assert abs(got / float(n) - 1.0) <= float(tol), (name, got, n)
+
+
+def _zero_params(cfg):
+    # read-only zero views of the real shapes: the wiring is exercised at the
+    # full widths without holding the weights in memory
+    return synth._walk(synth.unet_param_shapes(cfg), lambda p, s: np.broadcast_to(np.float32(0), s))
+
+
+def pin_unet_topology_from_the_pages():
+    """Every stage output of the oracle's U-Net has the channels and size of
+    the pages' topology diagrams (batch 0: shapes only)."""
+    rows = _golden("unet_topology.txt")
+    for key in ("sdxl_inpaint", "sd21"):
+        cfg = synth.UNET_CONFIGS[key]
+        want = {r[1]: tuple(int(v) for v in r[2:]) for r in rows if r[0] == key}
+        Cin, H, W = want["input"]
+        assert Cin == cfg.in_channels
+        rec = []
+        x = np.zeros((0, Cin, H, W))
+        ctx = np.zeros((0, 77, cfg.ctx_dim))
+        add = np.zeros((0, cfg.add_in)) if cfg.add_in else None
+        ou.unet_forward(x, np.zeros(0), ctx, _zero_params(cfg), cfg, add, rec)
+        got = {name: shape[1:] for name, shape in rec}
+        L = len(cfg.channels)
+        for lvl in range(L):
+            assert got[f"down{lvl}.{cfg.layers_per_block - 1}"] == want[f"down{lvl}"], (key, lvl)
+            assert got[f"up{lvl}"] == want[f"up{lvl}"], (key, lvl)
+        assert got["mid"] == want["mid"]
+        assert got["conv_out"] == want["output"]
+        # the skips the diagrams list: the last output kept at each level
+        for lvl in range(L):
+            assert got[f"down{lvl}.0"][0] == want[f"down{lvl}"][0]
+
+
+def pin_timestep_embedding():
+    """Sinusoidal embedding: t = 0 gives cosines 1 and sines 0; the first
+    frequency is 1 (entries cos t, sin t); e(t1) . e(t2) = sum_i cos((t1 -
+    t2) f_i) with f_i = 10000^(-i / half), so |e(t)|^2 = half."""
+    dim, half = 320, 160
+    e = ou.timestep_embedding(np.array([0.0, 1.0, 999.0, 500.5]), dim)
+    _close(e[0], np.r_[np.ones(half), np.zeros(half)], 0.0, "t = 0")
+    _close([e[2, 0], e[2, half]], [math.cos(999.0), math.sin(999.0)], 1e-12, "first frequency")
+    f = 10000.0 ** (-np.arange(half) / half)
+    _close(e[2] @ e[3], np.cos((999.0 - 500.5) * f).sum(), 1e-9, "shift identity")
+    _close((e * e).sum(axis=1), np.full(4, float(half)), 1e-9, "norm")
+
+
+def pin_unet_batch_independence():
+    cfg = synth.UNetConfig("pin_tiny", 4, 4, (64, 128), (1, 1), 1, 2, 64, add_in=32)
+    inp = synth.make_unet_inputs(cfg, 3, 2, 8, 8, weight_std=0.08, t=(999.0, 17.0))
+    y = ou.unet_forward(inp["x"], inp["t"], inp["ctx"], inp["params"], cfg, inp["add"])
+    for b in range(2):
+        yb = ou.unet_forward(inp["x"][b:b + 1], inp["t"][b:b + 1], inp["ctx"][b:b + 1],
+                             inp["params"], cfg, inp["add"][b:b + 1])
+        _close(y[b:b + 1], yb, 1e-12, f"sample {b} alone")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
