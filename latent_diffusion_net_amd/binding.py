@@ -40,7 +40,9 @@ EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_masked",
            "st_block_read_timing_launches", "st_measure_mfma_bf16",
            "st_group_norm_workspace_bytes", "st_group_norm", "st_group_norm_noalloc",
            "st_guided_ddpm_step", "st_resnet_create", "st_resnet_forward",
-           "st_resnet_check_range", "st_resnet_destroy")
+           "st_resnet_check_range", "st_resnet_destroy", "st_unet_create",
+           "st_unet_forward", "st_unet_device_bytes", "st_unet_check_range",
+           "st_unet_destroy")
 
 
 class LayerWeights(ctypes.Structure):
@@ -58,6 +60,24 @@ RESNET_FIELDS = ("gn1_w", "gn1_b", "conv1_w", "conv1_b", "temb_w", "temb_b", "gn
 
 class ResnetWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in RESNET_FIELDS]
+
+
+class UNetConfigC(ctypes.Structure):
+    _fields_ = [("in_channels", ctypes.c_int), ("out_channels", ctypes.c_int),
+                ("levels", ctypes.c_int), ("channels", ctypes.c_int * 4),
+                ("depths", ctypes.c_int * 4), ("mid_depth", ctypes.c_int),
+                ("layers_per_block", ctypes.c_int), ("ctx_dim", ctypes.c_int),
+                ("add_in", ctypes.c_int)]
+
+
+class UNetWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "time1_w", "time1_b", "time2_w", "time2_b", "add1_w", "add1_b", "add2_w", "add2_b",
+        "conv_in_w", "conv_in_b")] + [
+        ("resnets", ctypes.POINTER(ResnetWeights)), ("blocks", ctypes.POINTER(BlockWeights)),
+        ("down_w", ctypes.POINTER(ctypes.c_void_p)), ("down_b", ctypes.POINTER(ctypes.c_void_p)),
+        ("up_w", ctypes.POINTER(ctypes.c_void_p)), ("up_b", ctypes.POINTER(ctypes.c_void_p))] + [
+        (n, ctypes.c_void_p) for n in ("norm_out_w", "norm_out_b", "conv_out_w", "conv_out_b")]
 
 
 class Timing(ctypes.Structure):
@@ -131,6 +151,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_resnet_check_range.restype = i
     lib.st_resnet_destroy.argtypes = [vp]
     lib.st_resnet_destroy.restype = None
+    lib.st_unet_create.argtypes = [ctypes.POINTER(UNetConfigC), i, i, i, ctypes.POINTER(UNetWeights),
+                                   vp, ctypes.POINTER(vp)]
+    lib.st_unet_create.restype = i
+    lib.st_unet_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.st_unet_forward.restype = i
+    lib.st_unet_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.st_unet_device_bytes.restype = i
+    lib.st_unet_check_range.argtypes = [vp, vp]
+    lib.st_unet_check_range.restype = i
+    lib.st_unet_destroy.argtypes = [vp]
+    lib.st_unet_destroy.restype = None
     lib.st_group_norm_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f32, i, i, vp]
     lib.st_group_norm_noalloc.restype = i
     lib.st_guided_ddpm_step.argtypes = [vp, i, vp, vp, vp, ll, f32, i, i, dbl, dbl, vp]
@@ -305,6 +336,108 @@ class STResnet:
             self.close()
         except Exception:
             pass
+
+
+def _block_struct(bp, keep):
+    layers = (LayerWeights * max(len(bp["layers"]), 1))()
+    for li, lw in enumerate(bp["layers"]):
+        for n in LAYER_FIELDS:
+            setattr(layers[li], n, _ptr(lw.get(n)))
+    keep.append(layers)
+    bw = BlockWeights()
+    for n in BLOCK_FIELDS:
+        setattr(bw, n, _ptr(bp.get(n)))
+    bw.layers = ctypes.cast(layers, ctypes.POINTER(LayerWeights))
+    return bw
+
+
+class STUNet:
+    """One U-Net denoiser timestep (st_unet_*).  ``cfg``: a
+    ``synth.UNetConfig``; ``params``: the nested tree of
+    ``synth.unet_param_shapes`` holding device bf16 tensors.  The library
+    copies the weights."""
+
+    def __init__(self, cfg, B, H, W, params: Dict, stream=None):
+        self._lib = load_library()
+        self._h = None
+        self.cfg, self.shape = cfg, (B, H, W)
+        L = len(cfg.channels)
+        c = UNetConfigC()
+        c.in_channels, c.out_channels, c.levels = cfg.in_channels, cfg.out_channels, L
+        for i in range(L):
+            c.channels[i], c.depths[i] = cfg.channels[i], cfg.depths[i]
+        c.mid_depth, c.layers_per_block = cfg.mid_depth, cfg.layers_per_block
+        c.ctx_dim, c.add_in = cfg.ctx_dim, cfg.add_in
+        keep = []
+        res = [r for lv in params["down"] for r in lv["res"]] + params["mid"]["res"] + \
+              [r for lv in params["up"] for r in lv["res"]]
+        blk = [b for lv in params["down"] for b in lv["attn"]] + params["mid"]["attn"] + \
+              [b for lv in params["up"] for b in lv["attn"]]
+        rarr = (ResnetWeights * len(res))()
+        for i, r in enumerate(res):
+            for n in RESNET_FIELDS:
+                setattr(rarr[i], n, _ptr(r.get(n)))
+        barr = (BlockWeights * max(len(blk), 1))()
+        for i, b in enumerate(blk):
+            barr[i] = _block_struct(b, keep)
+        ptrs = lambda vals: (ctypes.c_void_p * max(len(vals), 1))(*[_ptr(v) for v in vals])
+        dw = ptrs([lv["down_w"] for lv in params["down"] if "down_w" in lv])
+        db = ptrs([lv["down_b"] for lv in params["down"] if "down_w" in lv])
+        uw = ptrs([lv["up_w"] for lv in params["up"] if "up_w" in lv])
+        ub = ptrs([lv["up_b"] for lv in params["up"] if "up_w" in lv])
+        w = UNetWeights()
+        for n in ("time1_w", "time1_b", "time2_w", "time2_b", "add1_w", "add1_b", "add2_w",
+                  "add2_b", "conv_in_w", "conv_in_b", "norm_out_w", "norm_out_b", "conv_out_w",
+                  "conv_out_b"):
+            setattr(w, n, _ptr(params.get(n)))
+        w.resnets = ctypes.cast(rarr, ctypes.POINTER(ResnetWeights))
+        w.blocks = ctypes.cast(barr, ctypes.POINTER(BlockWeights))
+        cv = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        w.down_w, w.down_b, w.up_w, w.up_b = cv(dw), cv(db), cv(uw), cv(ub)
+        handle = ctypes.c_void_p()
+        _check(self._lib.st_unet_create(ctypes.byref(c), B, H, W, ctypes.byref(w),
+                                        _stream_handle(stream), ctypes.byref(handle)))
+        self._h = handle
+
+    def forward(self, x, t, ctx, add=None, y=None, stream=None):
+        import torch
+        B, H, W = self.shape
+        if y is None:
+            y = torch.empty((B, self.cfg.out_channels, H, W), dtype=torch.bfloat16, device=x.device)
+        _check(self._lib.st_unet_forward(self._h, _ptr(x), _ptr(t), _ptr(ctx), _ptr(add), _ptr(y),
+                                         _stream_handle(stream)))
+        return y
+
+    def device_bytes(self) -> int:
+        n = ctypes.c_ulonglong()
+        _check(self._lib.st_unet_device_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def check_range(self, stream=None):
+        _check(self._lib.st_unet_check_range(self._h, _stream_handle(stream)))
+
+    def close(self):
+        if self._h is not None:
+            self._lib.st_unet_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tree_to_device(tree, device="cuda"):
+    """A nested dict / list of float32 arrays (None kept) -> device bf16 tensors."""
+    import torch
+    if isinstance(tree, dict):
+        return {k: tree_to_device(v, device) for k, v in tree.items()}
+    if isinstance(tree, list):
+        return [tree_to_device(v, device) for v in tree]
+    if tree is None:
+        return None
+    return torch.from_numpy(tree).to(device=device).to(torch.bfloat16).contiguous()
 
 
 def _dtype_code(t) -> int:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libst_block.so")
-SOURCES = ["host.hip", "k_norm.hip", "k_gemm.hip", "k_attn.hip", "k_probe.hip", "ops.hip", "resnet.hip"]
+SOURCES = ["host.hip", "k_norm.hip", "k_gemm.hip", "k_attn.hip", "k_probe.hip", "ops.hip", "resnet.hip", "unet.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -470,23 +470,25 @@ bool temb_proj_supported(int B, int Dt) {
 }
 
 // Convolution weights to the GEMM operand: w [Cout][Cin][3][3] (bf16) ->
-// dst [Cout][ldk] fp16 with dst[co][t * Cin + ci] = w[co][ci][t] (tap t = 3
-// di + dj), and, with a 1x1 shortcut, dst[co][9 Cin + ci] = sc[co][ci]
-// (bf16 [Cout][Csc]).  Magnitudes above 65504 set *overflow.
+// dst [Cout][ldk] fp16 with dst[co][t * Cp + ci] = w[co][ci][t] (tap t = 3
+// di + dj; channels Cin <= ci < Cp are zero: the padding of a narrow input
+// to a whole number of 64-deep K stages), and, with a 1x1 shortcut,
+// dst[co][9 Cp + ci] = sc[co][ci] (bf16 [Cout][Csc]).  Magnitudes above
+// 65504 set *overflow.
 __global__ void conv_weight_pack_kernel(const bf16_t* __restrict__ w, const bf16_t* __restrict__ sc,
-                                        f16_t* __restrict__ dst, int Cout, int Cin, int Csc,
+                                        f16_t* __restrict__ dst, int Cout, int Cin, int Cp, int Csc,
                                         int* __restrict__ overflow) {
-  const int ldk = 9 * Cin + Csc;
+  const int ldk = 9 * Cp + Csc;
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<long long>(Cout) * ldk) return;
   const int co = static_cast<int>(idx / ldk);
   const int k = static_cast<int>(idx - static_cast<long long>(co) * ldk);
-  float v;
-  if (k < 9 * Cin) {
-    const int t = k / Cin, ci = k - (k / Cin) * Cin;
-    v = bf2f(w[(static_cast<long long>(co) * Cin + ci) * 9 + t]);
+  float v = 0.f;
+  if (k < 9 * Cp) {
+    const int t = k / Cp, ci = k - (k / Cp) * Cp;
+    if (ci < Cin) v = bf2f(w[(static_cast<long long>(co) * Cin + ci) * 9 + t]);
   } else {
-    v = bf2f(sc[static_cast<long long>(co) * Csc + (k - 9 * Cin)]);
+    v = bf2f(sc[static_cast<long long>(co) * Csc + (k - 9 * Cp)]);
   }
   if (fabsf(v) > 65504.0f) *overflow = 1;
   dst[idx] = static_cast<f16_t>(v);
@@ -494,10 +496,167 @@ __global__ void conv_weight_pack_kernel(const bf16_t* __restrict__ w, const bf16
 
 hipError_t conv_weight_pack(const void* w, const void* sc, void* dst, int Cout, int Cin, int Csc,
                             int* overflow, hipStream_t s) {
-  const long long n = static_cast<long long>(Cout) * (9 * Cin + Csc);
+  return conv_weight_pack_padded(w, sc, dst, Cout, Cin, Cin, Csc, overflow, s);
+}
+
+hipError_t conv_weight_pack_padded(const void* w, const void* sc, void* dst, int Cout, int Cin,
+                                   int Cp, int Csc, int* overflow, hipStream_t s) {
+  if (Cp < Cin) return hipErrorInvalidValue;
+  const long long n = static_cast<long long>(Cout) * (9 * Cp + Csc);
   conv_weight_pack_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
       static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(sc), static_cast<f16_t*>(dst), Cout,
-      Cin, Csc, overflow);
+      Cin, Cp, Csc, overflow);
+  return hipGetLastError();
+}
+
+// NCHW bf16 -> the zero-haloed NHWC fp16 operand of a 3x3 convolution, no
+// normalisation: input pixel (i, j) goes to grid position (i + 1, j + 1)
+// (row (b * (Hg + 2) + i + 1) * Wp + j + 1, L elements per row), or, with
+// `up`, to the four positions (2i + a + 1, 2j + c + 1) of the 2x grid
+// (nearest-neighbour upsampling).  Channels C <= c < L are never written
+// (zero from allocation).  64 channels x 64 pixels per workgroup through
+// LDS, as the GroupNorm variant.
+__global__ __launch_bounds__(256) void nchw_to_pad_kernel(
+    const bf16_t* __restrict__ x, f16_t* __restrict__ out, int C, int H, int W, int Wp, int L,
+    int up, int* __restrict__ range_flag) {
+  __shared__ float tile[64][64 + 4];
+  const int N = H * W;
+  const int n0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = pass * 32 + (tid >> 3);
+    const int nl = 8 * (tid & 7);
+    const int c = c0 + cl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + nl + j;
+      tile[cl][nl + j] = (c < C && n < N) ? bf2f(x[(static_cast<long long>(b) * C + c) * N + n]) : 0.f;
+    }
+  }
+  __syncthreads();
+  const int Hg = up ? 2 * H : H;
+  const int cw = min(64, C - c0);  // channels of this tile
+  bool bad = false;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nl = pass * 32 + (tid >> 3);
+    const int cl = 8 * (tid & 7);
+    const int n = n0 + nl;
+    if (n >= N || cl >= cw) continue;
+    const int i = n / W, j = n - (n / W) * W;
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = tile[cl + q][nl];
+    const int reps = up ? 4 : 1;
+    for (int r = 0; r < reps; ++r) {
+      const int oi = up ? 2 * i + (r >> 1) : i, oj = up ? 2 * j + (r & 1) : j;
+      const long long row = (static_cast<long long>(b) * (Hg + 2) + oi + 1) * Wp + oj + 1;
+      f16_t* dst = out + row * L + c0 + cl;
+      if (cl + 8 <= cw) {
+        bad |= store8<f16_t>(dst, v);
+      } else {
+        for (int q = 0; q < cw - cl; ++q) {
+          dst[q] = static_cast<f16_t>(v[q]);
+          bad |= !(fabsf(v[q]) < 65520.f);
+        }
+      }
+    }
+  }
+  if (bad && range_flag) *range_flag = 1;
+}
+
+hipError_t nchw_to_pad(const void* x, void* out, int B, int C, int H, int W, int Wp, int L, bool up,
+                       int* range_flag, hipStream_t s) {
+  if (L % 8 || L < C) return hipErrorInvalidValue;
+  dim3 grid((H * W + 63) / 64, (C + 63) / 64, B);
+  nchw_to_pad_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<f16_t*>(out), C,
+                                          H, W, Wp, L, up ? 1 : 0, range_flag);
+  return hipGetLastError();
+}
+
+// Sinusoidal timestep embedding: out[b][i] = cos(t_b f_i), out[b][half + i]
+// = sin(t_b f_i), f_i = 10000^(-i / half), fp32.
+__global__ void timestep_embed_kernel(const float* __restrict__ t, float* __restrict__ out, int dim) {
+  const int b = blockIdx.x;
+  const int half = dim / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const float f = expf(-9.210340371976184f * static_cast<float>(i) / static_cast<float>(half));
+    float sv, cv;
+    sincosf(t[b] * f, &sv, &cv);
+    out[static_cast<long long>(b) * dim + i] = cv;
+    out[static_cast<long long>(b) * dim + half + i] = sv;
+  }
+}
+
+hipError_t timestep_embed(const float* t, float* out, int B, int dim, hipStream_t s) {
+  if (dim % 2) return hipErrorInvalidValue;
+  timestep_embed_kernel<<<B, 128, 0, s>>>(t, out, dim);
+  return hipGetLastError();
+}
+
+// One Linear of the embedding MLPs, tiny batch: y[b][o] = sum_d w[o][d]
+// act(x[b][d]) + bias[o] (+ y[b][o] when accumulating), act = SiLU or the
+// identity, x fp32 or bf16, w bf16 [Dout][Din]; with y16 the result is also
+// stored in bf16.  act(x) of every sample is staged in LDS once per
+// workgroup; one wavefront per output feature, 16-byte weight loads.
+template <typename TX>
+__global__ __launch_bounds__(256) void mlp_linear_kernel(
+    const TX* __restrict__ x, int silu, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ y, bf16_t* __restrict__ y16, int accumulate, int B, int Din, int Dout) {
+  extern __shared__ float sx[];  // [B][Din]
+  for (int i = threadIdx.x; i < B * Din; i += 256) {
+    const float v = to_f32<TX>(x[i]);
+    sx[i] = silu ? v / (1.0f + __expf(-v)) : v;
+  }
+  __syncthreads();
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (o >= Dout) return;
+  float acc[kTembMaxB];
+#pragma unroll
+  for (int b = 0; b < kTembMaxB; ++b) acc[b] = 0.f;
+  const bf16_t* wr = w + static_cast<long long>(o) * Din;
+  for (int d0 = lane * 8; d0 < Din; d0 += 512) {
+    float wv[8];
+    load8<bf16_t>(wr + d0, wv);
+#pragma unroll
+    for (int b = 0; b < kTembMaxB; ++b) {
+      if (b < B) {
+        const float* sb = sx + b * Din + d0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[b] = fmaf(wv[q], sb[q], acc[b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kTembMaxB; ++b) {
+    if (b < B) {
+      float v = warp_sum(acc[b]) + (bias ? bias[o] : 0.f);
+      if (lane == 0) {
+        const long long at = static_cast<long long>(b) * Dout + o;
+        if (accumulate) v += y[at];
+        y[at] = v;
+        if (y16) y16[at] = f2bf(v);
+      }
+    }
+  }
+}
+
+hipError_t mlp_linear(const void* x, bool x_bf16, bool silu, const void* w, const float* bias,
+                      float* y, void* y16, bool accumulate, int B, int Din, int Dout, hipStream_t s) {
+  if (!temb_proj_supported(B, Din)) return hipErrorInvalidValue;
+  const size_t lds = sizeof(float) * B * Din;
+  if (x_bf16)
+    mlp_linear_kernel<bf16_t><<<(Dout + 3) / 4, 256, lds, s>>>(
+        static_cast<const bf16_t*>(x), silu ? 1 : 0, static_cast<const bf16_t*>(w), bias, y,
+        static_cast<bf16_t*>(y16), accumulate ? 1 : 0, B, Din, Dout);
+  else
+    mlp_linear_kernel<float><<<(Dout + 3) / 4, 256, lds, s>>>(
+        static_cast<const float*>(x), silu ? 1 : 0, static_cast<const bf16_t*>(w), bias, y,
+        static_cast<bf16_t*>(y16), accumulate ? 1 : 0, B, Din, Dout);
   return hipGetLastError();
 }
 

@@ -218,6 +218,21 @@ bool temb_proj_supported(int B, int Dt);
 // -> tap-major fp16 GEMM operand [Cout][9 Cin + Csc].
 hipError_t conv_weight_pack(const void* w, const void* sc, void* dst, int Cout, int Cin, int Csc,
                             int* overflow, hipStream_t s);
+// The same with the input channels padded to Cp (>= Cin, zero weights).
+hipError_t conv_weight_pack_padded(const void* w, const void* sc, void* dst, int Cout, int Cin,
+                                   int Cp, int Csc, int* overflow, hipStream_t s);
+// U-Net helpers.  nchw_to_pad: NCHW bf16 x -> zero-haloed NHWC fp16 operand
+// (grid Hg = H or 2H with `up` (nearest 2x), rows (b (Hg + 2) + i + 1) Wp +
+// j + 1, L >= C elements per row, channels >= C untouched).
+hipError_t nchw_to_pad(const void* x, void* out, int B, int C, int H, int W, int Wp, int L, bool up,
+                       int* range_flag, hipStream_t s);
+// Sinusoidal embedding of t [B] (fp32) -> out [B][dim] fp32, cosines first.
+hipError_t timestep_embed(const float* t, float* out, int B, int dim, hipStream_t s);
+// y [B][Dout] (+)= w act(x) + bias for the embedding MLPs (x fp32 or bf16,
+// act SiLU or identity, w bf16 [Dout][Din]; y16 (optional) gets a bf16
+// copy); needs temb_proj_supported(B, Din).
+hipError_t mlp_linear(const void* x, bool x_bf16, bool silu, const void* w, const float* bias,
+                      float* y, void* y16, bool accumulate, int B, int Din, int Dout, hipStream_t s);
 // Key padding mask [B][nk] bytes (nonzero = attend) -> bits [B][4] words
 // (bit k of word w: key 32 w + k; keys >= nk clear); nk <= 96.
 hipError_t mask_to_bits(const uint8_t* mask, uint32_t* bits, int B, int nk, hipStream_t s);

@@ -259,3 +259,36 @@ def test_resnet_create_validates_before_any_device_call():
     assert lib.st_resnet_forward(None, P, P, P, None) == binding.ST_ERR_INVALID
     assert lib.st_resnet_check_range(None, None) == binding.ST_ERR_INVALID
     lib.st_resnet_destroy(None)
+
+
+def test_unet_create_validates_before_any_device_call():
+    lib = _lib()
+    c = binding.UNetConfigC()
+    c.in_channels, c.out_channels, c.levels = 4, 4, 2
+    c.channels[0], c.channels[1] = 64, 128
+    c.depths[0], c.depths[1] = 1, 1
+    c.mid_depth, c.layers_per_block, c.ctx_dim = 1, 2, 64
+    w = binding.UNetWeights()
+
+    def create(B=2, H=16, W=16, cc=c, ww=w):
+        h = ctypes.c_void_p()
+        st = lib.st_unet_create(ctypes.byref(cc) if cc is not None else None, B, H, W,
+                                ctypes.byref(ww) if ww is not None else None, None, ctypes.byref(h))
+        assert h.value is None
+        return st
+    assert create(cc=None) == binding.ST_ERR_INVALID
+    assert create(ww=None) == binding.ST_ERR_INVALID
+    assert create(B=5) == binding.ST_ERR_UNSUPPORTED
+    assert create(W=12) == binding.ST_ERR_UNSUPPORTED   # 12 / 2 = 6, not a multiple of 4
+    assert create() == binding.ST_ERR_INVALID            # weights missing
+    c.levels = 5
+    assert create() == binding.ST_ERR_INVALID
+    c.levels = 2
+    c.channels[1] = 100
+    assert create() == binding.ST_ERR_INVALID
+    c.channels[1] = 128
+    assert lib.st_unet_forward(None, 16, 16, 16, None, 16, None) == binding.ST_ERR_INVALID
+    n = ctypes.c_ulonglong()
+    assert lib.st_unet_device_bytes(None, ctypes.byref(n)) == binding.ST_ERR_INVALID
+    assert lib.st_unet_check_range(None, None) == binding.ST_ERR_INVALID
+    lib.st_unet_destroy(None)
