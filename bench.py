@@ -248,15 +248,94 @@ def resnet_flops(cfg) -> float:
     return f
 
 
-def next_rows(torch, cfg_block, blk_inputs, stream, reps=20):
-    """Measured rates of the parts built around the block: a ResnetBlock2D at
-    the bench stage, the GroupNorm(+SiLU) op, the guided DDPM step and the
-    block forward with a context key padding mask."""
-    from latent_diffusion_net_amd import STResnet, synth
-    from latent_diffusion_net_amd.binding import group_norm, guided_ddpm_step
-    out = {}
+def unet_flops(ucfg, B, H, W) -> float:
+    """Every convolution, ResnetBlock2D and transformer block of one U-Net
+    timestep (2 flops per multiply-add; the embedding MLPs left out)."""
+    from latent_diffusion_net_amd import synth
+    conv = lambda ci, co, h, w: 2.0 * B * h * w * co * 9 * ci
+    res = lambda ci, co, h, w: resnet_flops(synth.ResnetConfig("r", B, ci, co, h, w))
+    blk = lambda c, h, w, d: block_flops(synth.BlockConfig("b", B, c, h, w, c // 64, ucfg.ctx_dim, d, "bf16"))
+    L = len(ucfg.channels)
+    f = conv(ucfg.in_channels, ucfg.channels[0], H, W) + conv(ucfg.channels[0], ucfg.out_channels, H, W)
+    skips = synth.unet_skip_channels(ucfg)
+    ch, h, w = ucfg.channels[0], H, W
+    for l, c in enumerate(ucfg.channels):
+        for _ in range(ucfg.layers_per_block):
+            f += res(ch, c, h, w) + (blk(c, h, w, ucfg.depths[l]) if ucfg.depths[l] else 0.0)
+            ch = c
+        if l < L - 1:
+            f += conv(c, c, h // 2, w // 2)
+            h, w = h // 2, w // 2
+    f += 2 * res(ch, ch, h, w) + (blk(ch, h, w, ucfg.mid_depth) if ucfg.mid_depth else 0.0)
+    for l in reversed(range(L)):
+        c = ucfg.channels[l]
+        for _ in range(ucfg.layers_per_block + 1):
+            f += res(ch + skips.pop(), c, h, w) + (blk(c, h, w, ucfg.depths[l]) if ucfg.depths[l] else 0.0)
+            ch = c
+        if l > 0:
+            h, w = 2 * h, 2 * w
+            f += conv(c, c, h, w)
+    return f
+
+
+def unet_params_on_device(torch, ucfg, seed, dev):
+    """Random-init U-Net weights drawn on the GPU (N(0, 0.02^2) weights, zero
+    biases, unit norm gammas): for timing only, nothing is compared."""
+    from latent_diffusion_net_amd import synth
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    norm_w = ("gn1_w", "gn2_w", "gn_w", "norm_out_w", "ln1_w", "ln2_w", "ln3_w")
+
+    def draw(path, shape):
+        n = path[-1]
+        if n in norm_w:
+            return torch.ones(shape, dtype=torch.bfloat16, device=dev)
+        if n.endswith("_w"):
+            return (torch.randn(shape, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        return torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    return synth._walk(synth.unet_param_shapes(ucfg), draw)
+
+
+# The pages' run evidence: peak CUDA memory allocated for one denoiser
+# timestep at batch 1 (section 5 of each architecture page).
+PAGE_PEAK_GIB = {"sd21": 1.78, "sdxl_inpaint": 5.17}
+PAGE_LATENT = {"sd21": 96, "sdxl_inpaint": 128}
+
+
+def unet_row(torch, key, B, stream, reps=5):
+    from latent_diffusion_net_amd import STUNet, synth
     dev = "cuda:0"
-    # ResnetBlock2D at the SDXL Down1 stage (640 channels, 64 x 64, B = 2)
+    ucfg = synth.UNET_CONFIGS[key]
+    S = PAGE_LATENT[key]
+    p = unet_params_on_device(torch, ucfg, 7, dev)
+    weight_bytes = 2 * synth.unet_param_count(ucfg)
+    u = STUNet(ucfg, B, S, S, p)
+    del p
+    torch.cuda.empty_cache()
+    x = torch.randn(B, ucfg.in_channels, S, S, device=dev).to(torch.bfloat16)
+    ctx = torch.randn(B, 77, ucfg.ctx_dim, device=dev).to(torch.bfloat16)
+    add = torch.randn(B, ucfg.add_in, device=dev).to(torch.bfloat16) if ucfg.add_in else None
+    t = torch.full((B,), 999.0, device=dev)
+    y = torch.empty(B, ucfg.out_channels, S, S, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        u.forward(x, t, ctx, add, y, stream)
+    ms = _event_times(torch, lambda: u.forward(x, t, ctx, add, y, stream), reps, stream)
+    held = u.device_bytes()
+    u.close()
+    fl = unet_flops(ucfg, B, S, S)
+    r = _rate(ms, fl, "TFLOP/s", BF16_PEAK_TFLOPS)
+    r.update({"flops": fl, "bound": "mfma (convolutions, attention and GEMMs of every part)",
+              "device_gib_held": round(held / 2**30, 2),
+              "weights_gib_bf16": round(weight_bytes / 2**30, 2)})
+    if B == 1:
+        r["page_peak_allocated_gib_batch1"] = PAGE_PEAK_GIB[key]
+    return r
+
+
+def resnet_row(torch, stream, reps=20):
+    """ResnetBlock2D at the SDXL Down1 stage (640 channels, 64 x 64, B = 2)."""
+    from latent_diffusion_net_amd import STResnet, synth
+    dev = "cuda:0"
     rc = synth.ResnetConfig("sdxl_down1_640_64x64", 2, 640, 640, 64, 64)
     ri = synth.make_resnet_inputs(rc, 1)
     bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
@@ -268,9 +347,21 @@ def next_rows(torch, cfg_block, blk_inputs, stream, reps=20):
         res.forward(rx, rt, ry, stream)
     ms = _event_times(torch, lambda: res.forward(rx, rt, ry, stream), reps, stream)
     res.close()
-    out["F1 ResnetBlock2D (SDXL Down1, 640 ch, 64x64, B=2)"] = dict(
-        _rate(ms, resnet_flops(rc), "TFLOP/s", BF16_PEAK_TFLOPS), flops=resnet_flops(rc),
-        bound="mfma (the two 3x3 convolutions; GroupNorm passes and the time embedding inside)")
+    return dict(_rate(ms, resnet_flops(rc), "TFLOP/s", BF16_PEAK_TFLOPS), flops=resnet_flops(rc),
+                bound="mfma (the two 3x3 convolutions; GroupNorm passes and the time embedding inside)")
+
+
+def next_rows(torch, cfg_block, blk_inputs, stream, reps=20):
+    """Measured rates of the parts built around the block: a ResnetBlock2D at
+    the bench stage, the GroupNorm(+SiLU) op, the guided DDPM step and the
+    block forward with a context key padding mask."""
+    from latent_diffusion_net_amd import synth
+    from latent_diffusion_net_amd.binding import group_norm, guided_ddpm_step
+    out = {}
+    dev = "cuda:0"
+    out["F1 ResnetBlock2D (SDXL Down1, 640 ch, 64x64, B=2)"] = resnet_row(torch, stream, reps)
+    bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
+    rx = bf(synth.make_resnet_inputs(synth.ResnetConfig("gn", 2, 640, 640, 64, 64), 1)["x"])
     # GroupNorm + SiLU op on the same map: read once, write once at least
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
     gy = torch.empty_like(rx)
@@ -297,6 +388,9 @@ def next_rows(torch, cfg_block, blk_inputs, stream, reps=20):
     blk.forward_masked(x, ctx, m, y, stream)
     ms = _event_times(torch, lambda: blk.forward_masked(x, ctx, m, y, stream), reps, stream)
     ms0 = _event_times(torch, lambda: blk.forward(x, ctx, y, stream), reps, stream)
+    out["F2 U-Net timestep, SD2.1-base (96x96 latent, B=2 guidance pair)"] = unet_row(torch, "sd21", 2, stream)
+    out["F2 U-Net timestep, SD2.1-base (96x96 latent, B=1)"] = unet_row(torch, "sd21", 1, stream)
+    out["F2 U-Net timestep, SDXL-Inpaint (128x128 latent, B=1)"] = unet_row(torch, "sdxl_inpaint", 1, stream)
     out["F3 block forward with a context key mask (bench workload)"] = {
         "us_median": round(statistics.median(ms) * 1e3, 2),
         "us_median_unmasked_same_run": round(statistics.median(ms0) * 1e3, 2),
@@ -312,6 +406,8 @@ def main():
     ap.add_argument("--config", type=int, default=DEFAULT_WORKLOAD,
                     help="workload index (default: the SDXL Down1 block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=["resnet", "unet_sd21", "unet_sd21_b1", "unet_sdxl"],
+                    help="time only this part (for kernel traces) and print its row")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the ResnetBlock2D / GroupNorm / DDPM / masked-forward measurements")
     ap.add_argument("--kernels", action="store_true",
@@ -336,6 +432,16 @@ def main():
     import torch
     from latent_diffusion_net_amd import (STBlock, array_to_device,
                                           params_to_device, synth)
+    if args.part:
+        stream = torch.cuda.current_stream()
+        if args.part == "resnet":
+            row = resnet_row(torch, stream)
+        else:
+            key, B = {"unet_sd21": ("sd21", 2), "unet_sd21_b1": ("sd21", 1),
+                      "unet_sdxl": ("sdxl_inpaint", 1)}[args.part]
+            row = unet_row(torch, key, B, stream)
+        print(json.dumps({"part": args.part, **row}), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.config]
     inp = synth.make_inputs(cfg, synth.config_seed(args.config))

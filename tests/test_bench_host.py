@@ -155,3 +155,18 @@ def test_resnet_flops(bench):
     assert bench.resnet_flops(c) == 2.0 * n * 640 * 9 * 320 + 2.0 * n * 640 * 9 * 640 + 2.0 * n * 640 * 320
     c = synth.ResnetConfig("r", 2, 640, 640, 64, 64)
     assert bench.resnet_flops(c) == pytest.approx(120.8e9, rel=1e-3)
+
+
+def test_unet_flops_counts_every_part(bench):
+    """The U-Net flop count adds the parts' counts along the topology: for a
+    one-level U-Net it is conv_in + 2 ResNets + block + mid (2 ResNets +
+    block) + 3 up ResNets (+ blocks) + conv_out."""
+    from latent_diffusion_net_amd import synth
+    u = synth.UNetConfig("one", 4, 4, (64,), (1,), 1, 2, 64)
+    B, H, W = 2, 8, 8
+    conv = lambda ci, co: 2.0 * B * H * W * co * 9 * ci
+    res = lambda ci, co: bench.resnet_flops(synth.ResnetConfig("r", B, ci, co, H, W))
+    blk = bench.block_flops(synth.BlockConfig("b", B, 64, H, W, 1, 64, 1, "bf16"))
+    want = conv(4, 64) + conv(64, 4) + 2 * (res(64, 64) + blk) + 2 * res(64, 64) + blk \
+        + 3 * (res(128, 64) + blk)
+    assert bench.unet_flops(u, B, H, W) == pytest.approx(want)
