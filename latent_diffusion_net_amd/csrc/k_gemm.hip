@@ -712,14 +712,30 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   for (int j2 = 0; j2 < DPB; ++j2) {
     const int row = RPB * (wave * DPB + j2) + (lane >> 3);
     const int cl = (lane & 7) ^ ((row >> 1) & 7);
-    boff[j2] = static_cast<unsigned>((min(n0 + row, N - 1) * p.ldb + kz * kslice + cl * 8) * 2);
+    // a convolution's B operand takes its K position from the tap offsets
+    const int bk0 = EPI == EPI_CONV ? 0 : kz * kslice;
+    boff[j2] = static_cast<unsigned>((min(n0 + row, N - 1) * p.ldb + bk0 + cl * 8) * 2);
   }
   const int abytes = M * static_cast<int>(p.lda) * 2;
   const int bbytes = EPI == EPI_CONV ? static_cast<int>(p.conv.b_bytes) : N * static_cast<int>(p.ldb) * 2;
   // Convolution: the byte offset of K stage k within the activation buffer,
   // tracked incrementally (every caller asks for the stages in order, one
-  // at a time): tap ct = 3 di + dj at (crow, ccol), stage cj of the tap.
+  // at a time): tap ct = 3 di + dj at (crow, ccol), stage cj of the tap;
+  // a K slice of a split product starts at stage kz * kslice / 64.
   int ct = 0, cj = 0, crow = 0, ccol = 0;
+  if constexpr (EPI == EPI_CONV) {
+    const int s0 = kz * kslice / BKT;
+    const int taps = 9 * p.conv.spt;
+    if (s0 < taps) {
+      ct = s0 / p.conv.spt;
+      cj = s0 - ct * p.conv.spt;
+    } else {
+      ct = 9;
+      cj = s0 - taps;
+    }
+    crow = ct / 3;
+    ccol = ct - crow * 3;
+  }
   auto next_boff = [&](int k) -> int {
     if constexpr (EPI != EPI_CONV) {
       return k * BKT * 2;
@@ -961,8 +977,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     // this slice's product, plain fp32, into ws[kz]
     q.epi.kind = EPI_STORE_F32;
     q.epi.bias = nullptr;
-    q.epi.out_f32 = p.ws + static_cast<long long>(kz) * M * N;
-    q.epi.ldo = N;
+    // slices of rows ldws = N rounded up to 64 (whole 64-wide column blocks)
+    const int ldws = (N + 63) & ~63;
+    q.epi.out_f32 = p.ws + static_cast<long long>(kz) * M * ldws;
+    q.epi.ldo = ldws;
     q.epi.out_act = nullptr;
     q.epi.row_stats = nullptr;
   }
@@ -992,6 +1010,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   for (int z = 0; z < p.ksplit; ++z) acc += p.ws[z * mn + idx];
   const int row = static_cast<int>(idx / p.N);
   epi_store<EPI, bf16_t>(p.epi, row, static_cast<int>(idx - static_cast<long long>(row) * p.N), acc);
+}
+
+// Second pass of split-K for a convolution: a thread takes four
+// consecutive pixels of one output channel, adds the slices in order
+// (rows of N rounded up to 64), then the per-(sample, channel) term and the
+// residual, and stores the valid pixels NCHW as the EPI_CONV epilogue does.
+__global__ __launch_bounds__(256) void splitk_reduce_conv_kernel(GemmParams p) {
+  const ConvGemm& cv = p.conv;
+  const int ldws = (p.N + 63) & ~63;
+  const int per_row = ldws >> 2;
+  const long long g = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int c = static_cast<int>(g / per_row);
+  if (c >= p.M) return;
+  const int m0 = static_cast<int>(g - static_cast<long long>(c) * per_row) * 4;
+  if (m0 >= p.N) return;
+  const int per_b = cv.Hq * cv.Wp;
+  const int b = m0 / per_b;
+  const int rem = m0 - b * per_b;
+  const int i = rem / cv.Wp;
+  const int j = rem - i * cv.Wp;
+  if (i >= cv.Ho || j >= cv.Wo) return;
+  const long long mn = static_cast<long long>(p.M) * ldws;
+  const float* w = p.ws + static_cast<long long>(c) * ldws + m0;
+  float4 a = *reinterpret_cast<const float4*>(w);
+  for (int z = 1; z < p.ksplit; ++z) {
+    const float4 v = *reinterpret_cast<const float4*>(w + z * mn);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  const float add = cv.cadd[static_cast<long long>(b) * p.M + c];
+  float y0 = a.x + add, y1 = a.y + add, y2 = a.z + add, y3 = a.w + add;
+  const long long plane = static_cast<long long>(cv.Ho) * cv.Wo;
+  const long long off = (static_cast<long long>(b) * p.M + c) * plane + static_cast<long long>(i) * cv.Wo + j;
+  if (cv.resid) {
+    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(cv.resid) + off);
+    y0 += __uint_as_float(r.x << 16);
+    y1 += __uint_as_float(r.x & 0xffff0000u);
+    y2 += __uint_as_float(r.y << 16);
+    y3 += __uint_as_float(r.y & 0xffff0000u);
+  }
+  *reinterpret_cast<uint2*>(static_cast<bf16_t*>(cv.out) + off) = make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
 }
 
 // Second pass of split-K for the fp16 stream (EPI_STORE_H16 / EPI_RESID_H16):
@@ -1164,11 +1222,30 @@ static int cu_count() {
 // Convolutions: 128x128 tiles, two per CU (four-stage ring when there are no
 // more tiles than CUs), or 256x256 tiles when there are many of them.
 static hipError_t launch_conv(const GemmParams& p, hipStream_t s) {
+  if (p.ksplit > 1) {
+    // slices one 128x128 workgroup per CU (four-stage ring), then the sum
+    const long long wgs = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128) * p.ksplit;
+    hipError_t e = wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 4>(p, ACT_F16, EPI_CONV, p.ksplit, s)
+                                     : launch_pipe<2, 2, 2, 2, 2>(p, ACT_F16, EPI_CONV, p.ksplit, s);
+    if (e != hipSuccess) return e;
+    const long long n = static_cast<long long>(p.M) * (((p.N + 63) & ~63) >> 2);
+    splitk_reduce_conv_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
   const long long tiles = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128);
   const long long big = static_cast<long long>((p.M + 255) / 256) * ((p.N + 255) / 256);
   if (big >= kBigTileMin) return launch_pipe<2, 4, 4, 2, 1>(p, ACT_F16, EPI_CONV, 1, s);
   if (tiles <= cu_count()) return launch_pipe<2, 2, 2, 2, 1, 4>(p, ACT_F16, EPI_CONV, 1, s);
   return launch_pipe<2, 2, 2, 2, 2>(p, ACT_F16, EPI_CONV, 1, s);
+}
+
+int conv_ksplit(int M, int N, int K, int cus) {
+  const long long tiles = static_cast<long long>((M + 127) / 128) * ((N + 127) / 128);
+  if (2 * tiles > cus) return 1;
+  const int stages = K / 64;
+  for (int sp = 12; sp > 1; --sp)
+    if (stages % sp == 0 && stages / sp >= 16 && tiles * sp <= cus) return sp;
+  return 1;
 }
 
 hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
@@ -1194,7 +1271,8 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.K % 64) return hipErrorInvalidValue;
   if (p.epi.kind == EPI_CONV) {
     const ConvGemm& cv = p.conv;
-    if (op != ACT_F16 || p.ksplit > 1 || p.epi.ln_stats || !cv.cadd || !cv.out || cv.spt < 1 ||
+    if (op != ACT_F16 || (p.ksplit > 1 && (!p.ws || p.K % (p.ksplit * 64))) || p.epi.ln_stats ||
+        !cv.cadd || !cv.out || cv.spt < 1 ||
         cv.sc_spt < 0 || p.K != (9 * cv.spt + cv.sc_spt) * 64 || cv.Wp % 4 || cv.Wo % 4 ||
         cv.Wo > cv.Wp || cv.Ho > cv.Hq || p.N % (cv.Hq * cv.Wp) || cv.b_bytes <= 0 ||
         cv.b_bytes > 0x7fffffffLL || static_cast<long long>(p.M) * p.lda * 2 > 0x7fffffffLL)

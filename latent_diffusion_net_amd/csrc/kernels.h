@@ -136,6 +136,13 @@ struct GemmParams {
   ConvGemm conv;  // EPI_CONV only
 };
 
+// K slices for an implicit-GEMM convolution (M = Cout, N = pixels of the
+// padded grid, K = 9 Cin + Csc): with fewer than half as many 128x128
+// output tiles as CUs, the most slices (<= 12) that keep each at least 16
+// stages deep and give every slice a CU; 1 = no split.  Workspace of a
+// split product: ksplit * M * (N rounded up to 64) floats.
+int conv_ksplit(int M, int N, int K, int cus);
+
 // MFMA GEMM with 16-bit operands and fp32 accumulation.  `op` is ACT_BF16 or
 // ACT_F16 and gives the type of A and B.  Requires K % 64 == 0 and 16-byte
 // aligned rows; any M, N.

@@ -50,6 +50,8 @@ struct st_resnet {
   float2* part;
   void *p1, *p2, *h;
   int* range_flag;
+  int ks1, ks2;      // K slices of conv1 / conv2 (1 = none)
+  float* ws;         // their fp32 partial products
 };
 
 namespace {
@@ -119,7 +121,8 @@ bool overlaps(const void* a, size_t an, const void* c, size_t cn) {
 // The implicit-GEMM convolution over P (L elements per pixel row): A = the
 // packed weights, B = P shifted per tap (see ConvGemm).
 GemmParams conv_gemm(const st_resnet* r, const void* w, int K, const void* P, int L, int spt,
-                     int sc_spt, int sc_cbase, const float* cadd, const void* resid, void* out) {
+                     int sc_spt, int sc_cbase, const float* cadd, const void* resid, void* out,
+                     int ksplit) {
   GemmParams p{};
   p.A = w; p.lda = K;
   p.B = P; p.ldb = L;
@@ -131,6 +134,10 @@ GemmParams conv_gemm(const st_resnet* r, const void* w, int K, const void* P, in
   p.conv.spt = spt; p.conv.sc_spt = sc_spt; p.conv.sc_cbase = sc_cbase; p.conv.sc_roff = r->Wp + 1;
   p.conv.b_bytes = r->prows * L * 2;
   p.conv.cadd = cadd; p.conv.resid = resid; p.conv.out = out;
+  if (ksplit > 1) {
+    p.ksplit = ksplit;
+    p.ws = r->ws;
+  }
   return p;
 }
 
@@ -222,6 +229,18 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
   r->p2 = mk.alloc(static_cast<size_t>(prows) * L2 * 2, "conv2 operand map");
   r->h = mk.alloc(static_cast<size_t>(B) * Cout * H * W * 2, "intermediate h");
   r->range_flag = static_cast<int*>(mk.alloc(sizeof(int), "range flag"));
+  // convolutions with few output tiles split K (one slice per CU)
+  {
+    int cus = 0;
+    mk.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    const int N = B * (H + 2) * Wp;
+    r->ks1 = conv_ksplit(Cout, N, 9 * Cin, cus);
+    r->ks2 = conv_ksplit(Cout, N, 9 * Cout + Csc, cus);
+    const int most = r->ks1 > r->ks2 ? r->ks1 : r->ks2;
+    r->ws = most > 1 ? static_cast<float*>(mk.alloc(sizeof(float) * most * Cout * ((N + 63) / 64 * 64),
+                                                    "convolution partial products"))
+                     : nullptr;
+  }
   // the halos of P1 and P2 stay zero: no kernel writes them
   if (mk.ok()) mk.dev(hipMemsetAsync(r->p1, 0, static_cast<size_t>(prows) * Cin * 2, s), "clear P1");
   if (mk.ok()) mk.dev(hipMemsetAsync(r->p2, 0, static_cast<size_t>(prows) * L2 * 2, s), "clear P2");
@@ -273,7 +292,8 @@ ST_API st_status st_resnet_forward(st_resnet* r, const void* x, const void* temb
          "GroupNorm 1 + SiLU");
   RS_TRY(temb_proj(temb, r->temb_w, r->temb_b, r->conv1_b, r->cadd1, B, r->Dt, Cout, s),
          "time embedding");
-  RS_TRY(gemm_mfma(conv_gemm(r, r->w1, 9 * Cin, r->p1, Cin, Cin / 64, 0, 0, r->cadd1, nullptr, r->h),
+  RS_TRY(gemm_mfma(conv_gemm(r, r->w1, 9 * Cin, r->p1, Cin, Cin / 64, 0, 0, r->cadd1, nullptr, r->h,
+                             r->ks1),
                    ACT_F16, s),
          "conv1");
   RS_TRY(gn_stats(r->h, true, B, Cout, N, r->part, kMaxSplit, s), "GroupNorm 2 statistics");
@@ -281,7 +301,7 @@ ST_API st_status st_resnet_forward(st_resnet* r, const void* x, const void* temb
                       r->eps, nullptr, 0, 0, r->range_flag, s),
          "GroupNorm 2 + SiLU");
   RS_TRY(gemm_mfma(conv_gemm(r, r->w2, 9 * Cout + r->Csc, r->p2, r->L2, Cout / 64, r->Csc / 64, Cout,
-                             r->cadd2, r->Csc ? nullptr : x, y),
+                             r->cadd2, r->Csc ? nullptr : x, y, r->ks2),
                    ACT_F16, s),
          "conv2");
   return ST_OK;

@@ -42,10 +42,7 @@ struct Conv {
   float* cadd;         // [B][Cout]
   void* P;             // operand buffer, zero halo
   float *gn_w, *gn_b;  // conv_out's GroupNorm
-};
-
-struct Level {
-  std::vector<int> res, blk;  // indices into st_unet::res / ::blk
+  int ksplit;          // K slices (1 = none), partial products in st_unet::ws
 };
 
 }  // namespace
@@ -69,6 +66,7 @@ struct st_unet {
   std::vector<int> skip_h, skip_w;
   void *ta, *tb, *tc, *cat;       // work maps (bf16 NCHW, the largest size)
   int* range_flag;
+  float* ws;                      // split-K partial products of the convolutions
   unsigned long long bytes;
 };
 
@@ -192,6 +190,10 @@ hipError_t run_conv(st_unet* u, const Conv& c, const void* x, void* y, hipStream
   p.conv.spt = c.Cp / 64; p.conv.sc_spt = 0; p.conv.sc_cbase = 0; p.conv.sc_roff = c.Wp + 1;
   p.conv.b_bytes = c.prows * c.Cp * 2;
   p.conv.cadd = c.cadd; p.conv.resid = nullptr; p.conv.out = y;
+  if (c.ksplit > 1) {
+    p.ksplit = c.ksplit;
+    p.ws = u->ws;
+  }
   return gemm_mfma(p, ACT_F16, s);
 }
 
@@ -346,6 +348,20 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
   u->tb = mk.alloc(2ull * maxmap, "work map");
   u->tc = mk.alloc(2ull * maxmap, "work map");
   u->cat = mk.alloc(2ull * std::max(maxcat, maxmap), "concatenation");
+  // K slices of the convolutions with few output tiles, one workspace
+  {
+    int cus = 0;
+    mk.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+    long long wsf = 0;
+    for (Conv& cv : u->convs) {
+      const int Hq = cv.stride == 2 ? (cv.Hg + 2) / 2 : cv.Hg + 2;
+      const int N = B * Hq * cv.Wp;
+      cv.ksplit = conv_ksplit(cv.Cout, N, 9 * cv.Cp, cus);
+      if (cv.ksplit > 1)
+        wsf = std::max(wsf, static_cast<long long>(cv.ksplit) * cv.Cout * ((N + 63) / 64 * 64));
+    }
+    u->ws = wsf ? static_cast<float*>(mk.alloc(sizeof(float) * wsf, "convolution partial products")) : nullptr;
+  }
   if (mk.ok()) mk.dev(hipStreamSynchronize(s), "create: synchronise");
   if (mk.ok() && overflow) {
     int flag = 0;

@@ -63,6 +63,11 @@ CASES = [
     (synth.ResnetConfig("sd21_down0_320_96x96", 2, 320, 320, 96, 96), {}),
     # SDXL Up1's first ResNet: skip concatenated (1280 + 640 -> 640)
     (synth.ResnetConfig("sdxl_up1_1920to640_64x64", 2, 1920, 640, 64, 64), {}),
+    # SD2.1's 12 x 12 level at B = 1: 20 output tiles, the convolutions split
+    # over K (10 and 11 slices; the second product's slices reach into the
+    # 1x1-shortcut segment, 2560 -> 1280 channels)
+    (synth.ResnetConfig("sd21_up0_1280_12x12_b1", 1, 1280, 1280, 12, 12), {}),
+    (synth.ResnetConfig("sd21_up0_2560to1280_12x12_b1", 1, 2560, 1280, 12, 12), {}),
     # small and ragged: every bias, gamma and beta drawn; 5 rows, 8 columns
     (synth.ResnetConfig("b1_64to128_5x8", 1, 64, 128, 5, 8, Dt=32),
      dict(bias_std=0.1, norm_std=0.2, weight_std=0.05)),
