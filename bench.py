@@ -188,6 +188,41 @@ def summarize_pmc(fetch_csv, write_csv):
             "fetch_bytes": fetch_b, "write_bytes": write_b}
 
 
+def summarize_pmc_kernels(fetch_csv, write_csv, tcc_csv=None):
+    """Per kernel name: dispatches, mean FETCH_SIZE / WRITE_SIZE bytes per
+    dispatch scaled by the calibration copy, and (third CSV, a TCC_HIT_sum /
+    TCC_MISS_sum pass) the L2 hit rate."""
+    def rows(path):
+        return list(csv.DictReader(open(path)))
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in rows(path):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    fc = max((max(v) for k, v in fetch.items() if "copyBuffer" in k), default=float("nan"))
+    wc = max((max(v) for k, v in write.items() if "copyBuffer" in k), default=float("nan"))
+    kf, kw = COPY_BYTES / (fc * 1024.0), COPY_BYTES / (wc * 1024.0)
+    hit = per_kernel(tcc_csv, "TCC_HIT_sum") if tcc_csv else {}
+    miss = per_kernel(tcc_csv, "TCC_MISS_sum") if tcc_csv else {}
+    out = {"fetch_scale": kf, "write_scale": kw, "kernels": {}}
+    for k, v in fetch.items():
+        if "copyBuffer" in k:
+            continue
+        w = write.get(k, [])
+        e = {"dispatches": len(v),
+             "fetch_mb": sum(v) / len(v) * 1024.0 * kf / 1e6,
+             "write_mb": (sum(w) / len(w) * 1024.0 * kw / 1e6) if w else None}
+        if k in hit and k in miss:
+            h, m = sum(hit[k]), sum(miss[k])
+            e["l2_hit_rate"] = h / (h + m) if h + m > 0 else None
+        out["kernels"][k] = e
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -418,7 +453,16 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the self-attention HBM traffic from two "
                          "counter CSVs of --pmc-pass runs")
+    ap.add_argument("--summarize-pmc-kernels", nargs="+", metavar="CSV",
+                    help="per-kernel HBM bytes (and L2 hit rate) from the FETCH_SIZE "
+                         "and WRITE_SIZE (and TCC_HIT_sum/TCC_MISS_sum) CSVs of "
+                         "--pmc-pass runs")
     args = ap.parse_args()
+    if args.summarize_pmc_kernels:
+        if len(args.summarize_pmc_kernels) not in (2, 3):
+            ap.error("--summarize-pmc-kernels takes FETCH_CSV WRITE_CSV [TCC_CSV]")
+        print(json.dumps(summarize_pmc_kernels(*args.summarize_pmc_kernels), indent=1))
+        return
     if args.summarize_pmc:
         r = summarize_pmc(*args.summarize_pmc)
         r["kernel_source_sha256_16"] = source_hash()
