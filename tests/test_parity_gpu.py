@@ -139,7 +139,13 @@ def test_sharp_softmax(dtype, grid):
     # F = 2048 over few output tiles: FF2 takes the split-K path, so the
     # stream after each feed-forward comes from the ordered slice sum
     (1, 512, 9, 11, 8, 256),
-], ids=["b2_c128", "b1_c512_splitk"])
+    # 144 tokens per sample: the 128-row tiles of every product straddle the
+    # two samples, and 288 rows leave a ragged last tile
+    (2, 128, 12, 12, 2, 128),
+    # 320 channels: five K stages (an odd count) and output columns ragged
+    # over 128-wide tiles; 80 rows, one partial tile
+    (1, 320, 8, 10, 5, 128),
+], ids=["b2_c128", "b1_c512_splitk", "b2_c128_straddle", "b1_c320_odd_stages"])
 def test_stages_bf16(shape):
     """Residual stream after proj_in and after every sublayer."""
     B, C, H, W, heads, D_ctx = shape
@@ -154,6 +160,28 @@ def test_stages_bf16(shape):
         r = rel_l2(h, inter[key])
         _say(f"    stage {s} ({key}): rel_l2={r:.3e}")
         assert r <= 1e-2, (key, r)
+
+
+def test_groupnorm_offsets_and_scales():
+    """GroupNorm on an input whose channels carry offsets up to 30 and
+    spreads from 0.05 to 8 (the groups' means and variances differ widely):
+    h after proj_in against the oracle within what fp16 rounding of the
+    normalised operand and of h allows (each ~2^-12 relative, rel-L2 well
+    under 2e-3)."""
+    cfg = synth.BlockConfig("gn_offsets_c256_16x16", 2, 256, 16, 16, 4, 128, 1, "bf16")
+    inp = synth.make_inputs(cfg, 21, bias_std=0.05, norm_std=0.2)
+    rng = np.random.default_rng(22)
+    C = cfg.C
+    offset = rng.uniform(-30.0, 30.0, size=(1, C, 1, 1))
+    spread = np.exp(rng.uniform(np.log(0.05), np.log(8.0), size=(1, C, 1, 1)))
+    inp["x"] = synth.round_bf16((offset + spread * inp["x"]).astype(np.float32))
+    _, inter = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads,
+                                intermediates=True)
+    _, hs = run_gpu(cfg, inp, stages=[0])
+    h0 = inter["h0"]
+    r = rel_l2(hs[0].reshape(h0.shape), h0)
+    _say(f"    h0 rel_l2={r:.3e}")
+    assert r <= 2e-3, r
 
 
 def test_f32_tiny_config_exact():
