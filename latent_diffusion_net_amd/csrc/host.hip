@@ -39,6 +39,7 @@
 
 #include "../../include/st_block.h"
 #include "kernels.h"
+#include "parts.h"
 
 #define ST_API extern "C" __attribute__((visibility("default")))
 
@@ -109,6 +110,13 @@ struct st_block {
   void* wkv;  // [depth*2C][D]: per layer Wk2 rows then Wv2 rows
   float* bkv;
 
+  // buffers rewritten by every forward (ScratchPlan); bound to an arena of
+  // the handle's own, or to one shared with the other parts of a U-Net
+  ScratchPlan scratch;
+  void* scratch_own;
+  bool scratch_bound;
+  DevArena* persist;  // arena of the persistent allocations during create, or NULL
+
   float2* gn_part;
   int gn_max_split;
   void* u;
@@ -146,11 +154,17 @@ void* dalloc(st_block* b, size_t bytes) {
   if (bytes == 0) bytes = 16;
   bytes = static_cast<size_t>(round_up(static_cast<long long>(bytes), 256));
   if (b->bytes_cap && b->bytes_planned + bytes > b->bytes_cap) return nullptr;
+  if (b->persist && b->persist->base) {
+    void* p = b->persist->take(bytes);
+    if (p) b->bytes_planned += bytes;
+    return p;
+  }
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
+  if (b->persist) b->persist->count(bytes);
   b->bytes_planned += bytes;
   b->allocs.push_back(p);
   return p;
@@ -187,6 +201,11 @@ struct Creator {
     void* p = dalloc(b, bytes);
     if (!p) oom(what);
     return p;
+  }
+  // a buffer of the scratch arena (bound after create)
+  template <typename T>
+  void scr(T** field, size_t bytes) {
+    if (ok()) b->scratch.add(field, bytes);
   }
   // fp32 copy of a [n] vector given in the handle's dtype (NULL -> fill)
   float* vec(const void* src, long long n, float fill, const char* what) {
@@ -238,6 +257,19 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
                                  int D_ctx, int depth, st_dtype dtype,
                                  const st_block_weights* w, void* stream,
                                  st_block** out) {
+  return stb_block_create(B, C, H, W, heads, D_ctx, depth, dtype, w, stream, false, nullptr, out);
+}
+
+size_t stb_block_scratch_bytes(const st_block* b) { return b->scratch.bytes; }
+
+void stb_block_bind_scratch(st_block* b, void* base) {
+  b->scratch.bind(base);
+  b->scratch_bound = true;
+}
+
+st_status stb_block_create(int B, int C, int H, int W, int heads, int D_ctx, int depth, st_dtype dtype,
+                           const st_block_weights* w, void* stream, bool external_scratch,
+                           DevArena* persist, st_block** out) {
   g_err.clear();
   if (!out) return fail(ST_ERR_INVALID, "out is NULL");
   *out = nullptr;
@@ -301,6 +333,9 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->timing_mask = 0;
   b->range_flag = nullptr;
   b->key_bits = nullptr;
+  b->scratch_own = nullptr;
+  b->scratch_bound = false;
+  b->persist = persist;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Creator cr{b, s};
@@ -398,21 +433,34 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
 
   // Workspace.
   b->gn_max_split = 64;
-  b->gn_part = static_cast<float2*>(cr.alloc(sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split, "GroupNorm partials"));
-  b->u = cr.alloc(T * C * es, "normalised activations");
+  b->gn_part = nullptr; b->u = nullptr; b->h = nullptr; b->hcopy = nullptr; b->hstats = nullptr;
+  b->z = nullptr;
+  cr.scr(&b->gn_part, sizeof(float2) * B * ST_GN_GROUPS * b->gn_max_split);
+  cr.scr(&b->u, T * C * es);
   // the residual stream: fp32 on the fp32 path, fp16 (hcopy) on the bf16 path
-  b->h = b->bf16 ? nullptr : static_cast<float*>(cr.alloc(T * C * sizeof(float), "residual stream"));
-  b->hcopy = b->bf16 ? cr.alloc(T * static_cast<long long>(C) * es, "fp16 residual stream") : nullptr;
-  b->hstats = b->bf16 ? static_cast<float2*>(cr.alloc(T * static_cast<long long>(C / 64) * sizeof(float2),
-                                                      "residual stream statistics"))
-                      : nullptr;
+  if (b->bf16) {
+    cr.scr(&b->hcopy, T * static_cast<long long>(C) * es);
+    cr.scr(&b->hstats, T * static_cast<long long>(C / 64) * sizeof(float2));
+  } else {
+    cr.scr(&b->h, T * C * sizeof(float));
+  }
+  // Per-head Q / K / V^T: padding rows (N not a multiple of 128) are read by
+  // the attention kernels and must stay finite, so those buffers are the
+  // handle's own and cleared once; without padding rows they are scratch.
   const long long headbuf = static_cast<long long>(B) * heads * b->npad * 64 * es;
-  b->q = cr.alloc(headbuf, "Q");
-  b->k = cr.alloc(headbuf, "K");
-  b->vt = cr.alloc(headbuf, "V^T");
-  b->o = cr.alloc(T * C * es, "attention output");
-  b->f = cr.alloc(T * F * es, "GEGLU output");
-  b->z = b->bf16 ? nullptr : static_cast<float*>(cr.alloc(T * 2LL * F * sizeof(float), "FF1 output"));
+  const bool head_pad = b->npad != b->N;
+  if (head_pad) {
+    b->q = cr.alloc(headbuf, "Q");
+    b->k = cr.alloc(headbuf, "K");
+    b->vt = cr.alloc(headbuf, "V^T");
+  } else {
+    cr.scr(&b->q, headbuf);
+    cr.scr(&b->k, headbuf);
+    cr.scr(&b->vt, headbuf);
+  }
+  cr.scr(&b->o, T * C * es);
+  cr.scr(&b->f, T * F * es);
+  if (!b->bf16) cr.scr(&b->z, T * 2LL * F * sizeof(float));
   b->ctx_layer_stride = static_cast<long long>(B) * heads * b->cpad * 64;
   // The context K/V GEMM has only B*77 rows: with few output tiles it
   // splits K so that enough workgroups stream the weights.
@@ -427,10 +475,8 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
       for (int sp = 8; sp > 1; sp /= 2)
         if (D_ctx % (sp * 64) == 0 && tiles * sp <= cus) { b->ctx_ksplit = sp; break; }
     }
-    b->ctx_ws = b->ctx_ksplit > 1
-                    ? static_cast<float*>(cr.alloc(sizeof(float) * b->ctx_ksplit * ctx_rows * kvrows,
-                                                   "context K/V partial products"))
-                    : nullptr;
+    b->ctx_ws = nullptr;
+    if (b->ctx_ksplit > 1) cr.scr(&b->ctx_ws, sizeof(float) * b->ctx_ksplit * ctx_rows * kvrows);
   }
   // Self-attention load balance: with more query tiles than fit a whole
   // number per CU, the remainder is split over keys (ST_ATTN_CUS overrides
@@ -459,8 +505,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
       b->out_ksplit = slices(C);
       b->ff2_ksplit = slices(b->F);
       const int most = b->out_ksplit > b->ff2_ksplit ? b->out_ksplit : b->ff2_ksplit;
-      if (most > 1)
-        b->res_ws = static_cast<float*>(cr.alloc(sizeof(float) * most * T * C, "residual partial products"));
+      if (most > 1) cr.scr(&b->res_ws, sizeof(float) * most * T * C);
     }
     if (const char* e = std::getenv("ST_ATTN_CUS")) cus = std::atoi(e);
     attention_bf16_plan(B, heads, b->N, b->N, cus, b->attn_n_full, b->attn_nsplit);
@@ -468,9 +513,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
       const long long split_tiles =
           static_cast<long long>(B) * heads * ((b->N + attention_bf16_q_tile() - 1) / attention_bf16_q_tile()) -
           b->attn_n_full;
-      b->attn_part = static_cast<float*>(cr.alloc(
-          sizeof(float) * split_tiles * b->attn_nsplit * attention_bf16_part_floats(),
-          "self-attention partial results"));
+      cr.scr(&b->attn_part, sizeof(float) * split_tiles * b->attn_nsplit * attention_bf16_part_floats());
     }
   }
   b->key_bits = static_cast<uint32_t*>(cr.alloc(sizeof(uint32_t) * 4 * B, "context key mask"));
@@ -478,10 +521,19 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
   b->vct = cr.alloc(b->ctx_layer_stride * depth * es, "context V^T");
   // Padding rows of the per-head buffers are read by the attention kernels
   // and must hold finite values; no kernel ever writes them.
-  if (cr.ok()) {
+  if (cr.ok() && head_pad) {
     cr.dev(hipMemsetAsync(b->q, 0, headbuf, s), "clear Q");
     cr.dev(hipMemsetAsync(b->k, 0, headbuf, s), "clear K");
     cr.dev(hipMemsetAsync(b->vt, 0, headbuf, s), "clear V^T");
+  }
+  if (!external_scratch && cr.ok()) {
+    void* arena = cr.alloc(b->scratch.bytes, "workspace");
+    if (arena) {
+      b->scratch_own = arena;
+      stb_block_bind_scratch(b, arena);
+    }
+  }
+  if (cr.ok()) {
     cr.dev(hipMemsetAsync(b->kc, 0, b->ctx_layer_stride * depth * es, s), "clear context K");
     cr.dev(hipMemsetAsync(b->vct, 0, b->ctx_layer_stride * depth * es, s), "clear context V^T");
   }
@@ -501,6 +553,7 @@ ST_API st_status st_block_create(int B, int C, int H, int W, int heads,
     delete b;
     return fail(cr.st, cr.msg);
   }
+  b->persist = nullptr;  // create is over: nothing more is taken from it
   *out = b;
   return ST_OK;
 }
@@ -565,6 +618,7 @@ GemmParams gemm(const void* A, long long lda, const void* Bm, long long ldb,
 
 st_status forward_impl(st_block* b, const void* x, const void* ctx, const uint8_t* ctx_mask,
                        void* y, int stop_stage, float* h_out, hipStream_t s) {
+  if (!b->scratch_bound) return fail(ST_ERR_INVALID, "the handle's workspace is not bound");
   const bool bf = b->bf16;
   const int B = b->B, C = b->C, N = b->N, T = b->T, F = b->F, D = b->D;
   // 16-bit path operand types: fp16 where an activation produced by a norm

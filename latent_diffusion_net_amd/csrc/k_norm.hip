@@ -308,10 +308,35 @@ hipError_t gn_apply_nchw(const void* x, bool bf16, const float2* partial, int ma
 }
 
 // ------------------------------------------- convolution operand (NHWC)
+// The halo of a zero-haloed NHWC operand over an Hg x Wg grid: the pixels a
+// 3x3 convolution of stride 1 or 2 reads outside the image, i.e. padded
+// rows 0 and Hg + 1 (columns 0 .. Wg + 1) and padded columns 0 and Wg + 1
+// of rows 1 .. Hg: 2 (Wg + 2) + 2 Hg pixels per sample.  Columns past Wg + 1
+// (the rounding of Wp) and the rows after the last sample are read only for
+// the padding outputs the GEMM epilogue drops.  Halo pixel k of sample b:
+__device__ __forceinline__ long long halo_row(int b, int k, int Hg, int Wg, int Wp) {
+  int ip, jp;
+  if (k < Wg + 2) {
+    ip = 0; jp = k;
+  } else if (k < 2 * (Wg + 2)) {
+    ip = Hg + 1; jp = k - (Wg + 2);
+  } else {
+    const int q = k - 2 * (Wg + 2);
+    ip = 1 + (q >> 1);
+    jp = (q & 1) ? Wg + 1 : 0;
+  }
+  return (static_cast<long long>(b) * (Hg + 2) + ip) * Wp + jp;
+}
+__host__ __device__ inline int halo_pixels(int Hg, int Wg) { return 2 * (Wg + 2) + 2 * Hg; }
+// Workgroups past the image's pixel tiles write the halo's zeros: 32 halo
+// pixels x 64 channels each, 16 bytes per thread.
+constexpr int kHaloPerGroup = 32;
+
 // GroupNorm apply + SiLU from NCHW into the zero-haloed NHWC operand of a
 // 3x3 convolution: input pixel (i, j) of sample b goes to row (b * (H + 2) +
-// i + 1) * Wp + j + 1 of `out` (L fp16 elements per row, channels from 0);
-// the halo rows and columns are never written (zero from allocation).
+// i + 1) * Wp + j + 1 of `out` (L fp16 elements per row, channels from 0),
+// and the workgroups after the pixel tiles write the halo's zeros for the
+// same channels, so that the buffer needs no clearing beforehand.
 // Optionally the raw input also goes to `raw` (same rows, row length L_raw,
 // channels from raw_cbase): the operand of a fused 1x1 shortcut.  A
 // workgroup owns 64 channels x 64 pixels of one sample, transposed through
@@ -331,6 +356,16 @@ __global__ __launch_bounds__(256) void gn_apply_pad_kernel(
   const int b = blockIdx.z;
   const int cg = C / kGroups;
   const int tid = threadIdx.x;
+  const int ntiles = (N + 63) / 64;
+  if (static_cast<int>(blockIdx.x) >= ntiles) {  // halo zeros (no barrier below)
+    const int k = (blockIdx.x - ntiles) * kHaloPerGroup + (tid >> 3);
+    if (k >= halo_pixels(H, W)) return;
+    const long long row = halo_row(b, k, H, W, Wp);
+    const int cl = 8 * (tid & 7);
+    *reinterpret_cast<uint4*>(out + row * L + c0 + cl) = make_uint4(0u, 0u, 0u, 0u);
+    if (raw) *reinterpret_cast<uint4*>(raw + row * L_raw + raw_cbase + c0 + cl) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   if (tid < 64) {
     const int c = c0 + tid;
     const int g = b * kGroups + c / cg;
@@ -402,7 +437,7 @@ hipError_t gn_apply_pad(const void* x, const float2* partial, int max_split, con
   if (C % 64 || L % 8 || L_raw % 8 || raw_cbase % 8) return hipErrorInvalidValue;
   const int N = H * W;
   const int split = gn_split(C, N, max_split);
-  dim3 grid((N + 63) / 64, C / 64, B);
+  dim3 grid((N + 63) / 64 + (halo_pixels(H, W) + kHaloPerGroup - 1) / kHaloPerGroup, C / 64, B);
   gn_apply_pad_kernel<bf16_t><<<grid, 256, 0, s>>>(
       static_cast<const bf16_t*>(x), partial, split, gamma, beta, static_cast<f16_t*>(out), C, H,
       W, Wp, L, eps, static_cast<f16_t*>(raw), L_raw, raw_cbase, range_flag);
@@ -513,9 +548,10 @@ hipError_t conv_weight_pack_padded(const void* w, const void* sc, void* dst, int
 // normalisation: input pixel (i, j) goes to grid position (i + 1, j + 1)
 // (row (b * (Hg + 2) + i + 1) * Wp + j + 1, L elements per row), or, with
 // `up`, to the four positions (2i + a + 1, 2j + c + 1) of the 2x grid
-// (nearest-neighbour upsampling).  Channels C <= c < L are never written
-// (zero from allocation).  64 channels x 64 pixels per workgroup through
-// LDS, as the GroupNorm variant.
+// (nearest-neighbour upsampling).  Channels C <= c < L get zeros, and the
+// workgroups after the pixel tiles write the halo's zeros (all L channels),
+// so that the buffer needs no clearing beforehand.  64 channels x 64
+// pixels per workgroup through LDS, as the GroupNorm variant.
 __global__ __launch_bounds__(256) void nchw_to_pad_kernel(
     const bf16_t* __restrict__ x, f16_t* __restrict__ out, int C, int H, int W, int Wp, int L,
     int up, int* __restrict__ range_flag) {
@@ -525,6 +561,15 @@ __global__ __launch_bounds__(256) void nchw_to_pad_kernel(
   const int c0 = blockIdx.y * 64;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int Hg = up ? 2 * H : H, Wg = up ? 2 * W : W;
+  const int ntiles = (N + 63) / 64;
+  if (static_cast<int>(blockIdx.x) >= ntiles) {  // halo zeros (no barrier below)
+    const int k = (blockIdx.x - ntiles) * kHaloPerGroup + (tid >> 3);
+    const int cl = 8 * (tid & 7);
+    if (k >= halo_pixels(Hg, Wg) || c0 + cl >= L) return;
+    *reinterpret_cast<uint4*>(out + halo_row(b, k, Hg, Wg, Wp) * L + c0 + cl) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int cl = pass * 32 + (tid >> 3);
@@ -537,15 +582,14 @@ __global__ __launch_bounds__(256) void nchw_to_pad_kernel(
     }
   }
   __syncthreads();
-  const int Hg = up ? 2 * H : H;
-  const int cw = min(64, C - c0);  // channels of this tile
   bool bad = false;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int nl = pass * 32 + (tid >> 3);
     const int cl = 8 * (tid & 7);
     const int n = n0 + nl;
-    if (n >= N || cl >= cw) continue;
+    // channels past C hold zeros in the tile
+    if (n >= N || c0 + cl >= L) continue;
     const int i = n / W, j = n - (n / W) * W;
     float v[8];
 #pragma unroll
@@ -554,15 +598,7 @@ __global__ __launch_bounds__(256) void nchw_to_pad_kernel(
     for (int r = 0; r < reps; ++r) {
       const int oi = up ? 2 * i + (r >> 1) : i, oj = up ? 2 * j + (r & 1) : j;
       const long long row = (static_cast<long long>(b) * (Hg + 2) + oi + 1) * Wp + oj + 1;
-      f16_t* dst = out + row * L + c0 + cl;
-      if (cl + 8 <= cw) {
-        bad |= store8<f16_t>(dst, v);
-      } else {
-        for (int q = 0; q < cw - cl; ++q) {
-          dst[q] = static_cast<f16_t>(v[q]);
-          bad |= !(fabsf(v[q]) < 65520.f);
-        }
-      }
+      bad |= store8<f16_t>(out + row * L + c0 + cl, v);
     }
   }
   if (bad && range_flag) *range_flag = 1;
@@ -570,8 +606,10 @@ __global__ __launch_bounds__(256) void nchw_to_pad_kernel(
 
 hipError_t nchw_to_pad(const void* x, void* out, int B, int C, int H, int W, int Wp, int L, bool up,
                        int* range_flag, hipStream_t s) {
-  if (L % 8 || L < C) return hipErrorInvalidValue;
-  dim3 grid((H * W + 63) / 64, (C + 63) / 64, B);
+  // the channel tiles cover [0, L): L is C rounded up to at most 64
+  if (L % 8 || L < C || L > (C + 63) / 64 * 64) return hipErrorInvalidValue;
+  const int Hg = up ? 2 * H : H, Wg = up ? 2 * W : W;
+  dim3 grid((H * W + 63) / 64 + (halo_pixels(Hg, Wg) + kHaloPerGroup - 1) / kHaloPerGroup, (C + 63) / 64, B);
   nchw_to_pad_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<f16_t*>(out), C,
                                           H, W, Wp, L, up ? 1 : 0, range_flag);
   return hipGetLastError();

@@ -16,7 +16,8 @@
 // border of one pixel and Wp = W + 2 rounded up to 4 columns, so that every
 // tap of the 3x3 convolution is the same GEMM operand shifted by a whole
 // number of rows (the GEMM computes the padding columns too and discards
-// them in its epilogue).
+// them in its epilogue); the GroupNorm passes write the border's zeros too,
+// so the maps live in the scratch arena.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,6 +29,7 @@
 
 #include "../../include/st_resnet.h"
 #include "kernels.h"
+#include "parts.h"
 
 #define ST_API extern "C" __attribute__((visibility("default")))
 
@@ -52,6 +54,11 @@ struct st_resnet {
   int* range_flag;
   int ks1, ks2;      // K slices of conv1 / conv2 (1 = none)
   float* ws;         // their fp32 partial products
+  // part, h, cadd1, p1, p2 and ws are rewritten by every forward (ScratchPlan)
+  ScratchPlan scratch;
+  void* scratch_own;
+  bool scratch_bound;
+  DevArena* persist;  // arena of the persistent allocations during create, or NULL
 };
 
 namespace {
@@ -80,14 +87,21 @@ struct Maker {
   }
   void* alloc(size_t bytes, const char* what) {
     if (!ok()) return nullptr;
+    if (!bytes) bytes = 16;
     void* p = nullptr;
-    if (hipMalloc(&p, bytes ? bytes : 16) != hipSuccess) {
+    if (r->persist && r->persist->base) {
+      p = r->persist->take(bytes);
+    } else if (hipMalloc(&p, bytes) == hipSuccess) {
+      r->allocs.push_back(p);
+      if (r->persist) r->persist->count(bytes);
+    } else {
       (void)hipGetLastError();
+      p = nullptr;
+    }
+    if (!p) {
       st = ST_ERR_OUT_OF_MEMORY;
       msg = std::string("out of device memory allocating ") + what;
-      return nullptr;
     }
-    r->allocs.push_back(p);
     return p;
   }
   float* vec(const void* src, long long n, float fill, const char* what) {
@@ -146,6 +160,19 @@ GemmParams conv_gemm(const st_resnet* r, const void* w, int K, const void* P, in
 ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt, float eps,
                                   st_dtype dtype, const st_resnet_weights* w, void* stream,
                                   st_resnet** out) {
+  return stb_resnet_create(B, Cin, Cout, H, W, Dt, eps, dtype, w, stream, false, nullptr, out);
+}
+
+size_t stb_resnet_scratch_bytes(const st_resnet* r) { return r->scratch.bytes; }
+
+void stb_resnet_bind_scratch(st_resnet* r, void* base) {
+  r->scratch.bind(base);
+  r->scratch_bound = true;
+}
+
+st_status stb_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt, float eps, st_dtype dtype,
+                            const st_resnet_weights* w, void* stream, bool external_scratch,
+                            DevArena* persist, st_resnet** out) {
   st_set_error(ST_OK, "");
   if (!out) return fail(ST_ERR_INVALID, "out is NULL");
   *out = nullptr;
@@ -183,6 +210,9 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
   if (!r) return fail(ST_ERR_OUT_OF_MEMORY, "host allocation failed");
   r->B = B; r->Cin = Cin; r->Cout = Cout; r->H = H; r->W = W; r->Dt = Dt; r->Csc = Csc;
   r->eps = eps; r->device = dev; r->Wp = Wp; r->prows = prows; r->L2 = static_cast<int>(L2);
+  r->scratch_own = nullptr;
+  r->scratch_bound = false;
+  r->persist = persist;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Maker mk{r, s};
   r->gn1_w = mk.vec(w->gn1_w, Cin, 1.f, "gn1_w");
@@ -204,7 +234,7 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
   if (mk.ok()) mk.dev(conv_weight_pack(w->conv2_w, Csc ? w->sc_w : nullptr, r->w2, Cout, Cout, Csc, overflow, s),
                       "pack conv2");
   // conv2 adds its bias and the shortcut's, the same for every sample
-  r->cadd1 = static_cast<float*>(mk.alloc(sizeof(float) * B * Cout, "cadd1"));
+  r->scratch.add(&r->cadd1, sizeof(float) * B * Cout);  // written by every forward
   r->cadd2 = static_cast<float*>(mk.alloc(sizeof(float) * B * Cout, "cadd2"));
   if (mk.ok()) {
     for (int b = 0; b < B && mk.ok(); ++b) {
@@ -224,10 +254,11 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
                         "cadd2");
     if (mk.ok()) mk.dev(hipStreamSynchronize(s), "cadd2");
   }
-  r->part = static_cast<float2*>(mk.alloc(sizeof(float2) * B * ST_GN_GROUPS * kMaxSplit, "GroupNorm partials"));
-  r->p1 = mk.alloc(static_cast<size_t>(prows) * Cin * 2, "conv1 operand map");
-  r->p2 = mk.alloc(static_cast<size_t>(prows) * L2 * 2, "conv2 operand map");
-  r->h = mk.alloc(static_cast<size_t>(B) * Cout * H * W * 2, "intermediate h");
+  r->scratch.add(&r->part, sizeof(float2) * B * ST_GN_GROUPS * kMaxSplit);
+  // the operand maps: every forward writes their pixels and their halo
+  r->scratch.add(&r->p1, static_cast<size_t>(prows) * Cin * 2);
+  r->scratch.add(&r->p2, static_cast<size_t>(prows) * L2 * 2);
+  r->scratch.add(&r->h, static_cast<size_t>(B) * Cout * H * W * 2);
   r->range_flag = static_cast<int*>(mk.alloc(sizeof(int), "range flag"));
   // convolutions with few output tiles split K (one slice per CU)
   {
@@ -237,13 +268,16 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
     r->ks1 = conv_ksplit(Cout, N, 9 * Cin, cus);
     r->ks2 = conv_ksplit(Cout, N, 9 * Cout + Csc, cus);
     const int most = r->ks1 > r->ks2 ? r->ks1 : r->ks2;
-    r->ws = most > 1 ? static_cast<float*>(mk.alloc(sizeof(float) * most * Cout * ((N + 63) / 64 * 64),
-                                                    "convolution partial products"))
-                     : nullptr;
+    r->ws = nullptr;
+    if (most > 1) r->scratch.add(&r->ws, sizeof(float) * most * Cout * ((N + 63) / 64 * 64));
   }
-  // the halos of P1 and P2 stay zero: no kernel writes them
-  if (mk.ok()) mk.dev(hipMemsetAsync(r->p1, 0, static_cast<size_t>(prows) * Cin * 2, s), "clear P1");
-  if (mk.ok()) mk.dev(hipMemsetAsync(r->p2, 0, static_cast<size_t>(prows) * L2 * 2, s), "clear P2");
+  if (!external_scratch && mk.ok()) {
+    void* arena = mk.alloc(r->scratch.bytes, "workspace");
+    if (arena) {
+      r->scratch_own = arena;
+      stb_resnet_bind_scratch(r, arena);
+    }
+  }
   if (mk.ok()) mk.dev(hipMemsetAsync(r->range_flag, 0, sizeof(int), s), "range flag");
   if (mk.ok()) mk.dev(hipStreamSynchronize(s), "create: synchronise");
   if (mk.ok() && overflow) {
@@ -261,6 +295,7 @@ ST_API st_status st_resnet_create(int B, int Cin, int Cout, int H, int W, int Dt
     delete r;
     return fail(mk.st, mk.msg);
   }
+  r->persist = nullptr;  // create is over: nothing more is taken from it
   *out = r;
   return ST_OK;
 }
@@ -282,6 +317,7 @@ ST_API st_status st_resnet_forward(st_resnet* r, const void* x, const void* temb
   const size_t yb = static_cast<size_t>(r->B) * r->Cout * r->H * r->W * 2;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, temb, static_cast<size_t>(r->B) * r->Dt * 2))
     return fail(ST_ERR_INVALID, "y overlaps x or temb");
+  if (!r->scratch_bound) return fail(ST_ERR_INVALID, "the handle's workspace is not bound");
   DeviceGuard g(r->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "select device");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -20,6 +20,7 @@
 
 #include "../../include/st_unet.h"
 #include "kernels.h"
+#include "parts.h"
 
 #define ST_API extern "C" __attribute__((visibility("default")))
 
@@ -40,7 +41,7 @@ struct Conv {
   long long prows;
   void* w;             // fp16 [Cout][9 Cp]
   float* cadd;         // [B][Cout]
-  void* P;             // operand buffer, zero halo
+  void* P;             // operand buffer, zero halo (scratch)
   float *gn_w, *gn_b;  // conv_out's GroupNorm
   int ksplit;          // K slices (1 = none), partial products in st_unet::ws
 };
@@ -67,6 +68,13 @@ struct st_unet {
   void *ta, *tb, *tc, *cat;       // work maps (bf16 NCHW, the largest size)
   int* range_flag;
   float* ws;                      // split-K partial products of the convolutions
+  // The parts run one after another on one stream, so the buffers that each
+  // rewrites in every forward (its ScratchPlan) and the U-Net's own (the
+  // convolutions' GroupNorm partials and split-K products) share one arena
+  // of the largest plan's size.
+  ScratchPlan scratch;
+  void* arena;
+  DevArena* persist;  // arena of the persistent allocations during create
   unsigned long long bytes;
 };
 
@@ -101,14 +109,21 @@ struct Maker {
   }
   void* alloc(size_t bytes, const char* what) {
     if (!ok()) return nullptr;
+    if (!bytes) bytes = 16;
     void* p = nullptr;
-    if (hipMalloc(&p, bytes ? bytes : 16) != hipSuccess) {
+    if (u->persist && u->persist->base) {
+      p = u->persist->take(bytes);
+    } else if (hipMalloc(&p, bytes) == hipSuccess) {
+      u->allocs.push_back(p);
+      if (u->persist) u->persist->count(bytes);
+    } else {
       (void)hipGetLastError();
+      p = nullptr;
+    }
+    if (!p) {
       st = ST_ERR_OUT_OF_MEMORY;
       msg = std::string("out of device memory allocating ") + what;
-      return nullptr;
     }
-    u->allocs.push_back(p);
     return p;
   }
   float* vec(const void* src, long long n, float fill, const char* what) {
@@ -121,7 +136,8 @@ struct Maker {
     if (d) dev(hipMemcpyAsync(d, src, bytes, hipMemcpyDeviceToDevice, s), what);
     return d;
   }
-  // a convolution layer: weights packed, operand buffer zeroed
+  // a convolution layer: weights packed (its operand map is scratch,
+  // placed once the list of layers is complete)
   Conv conv(const void* w, const void* b, int Cin, int Cout, int Hi, int Wi, int stride, int up,
             int gn, const void* gn_w, const void* gn_b, int* overflow, const char* what) {
     Conv c{};
@@ -140,8 +156,7 @@ struct Maker {
         dev(hipMemcpyAsync(c.cadd + static_cast<long long>(i) * Cout, bias, sizeof(float) * Cout,
                            hipMemcpyDeviceToDevice, s), what);
     }
-    c.P = alloc(static_cast<size_t>(c.prows) * c.Cp * 2, what);
-    if (c.P) dev(hipMemsetAsync(c.P, 0, static_cast<size_t>(c.prows) * c.Cp * 2, s), what);
+    c.P = nullptr;
     if (gn) {
       c.gn_w = vec(gn_w, Cin, 1.f, what);
       c.gn_b = vec(gn_b, Cin, 0.f, what);
@@ -197,6 +212,9 @@ hipError_t run_conv(st_unet* u, const Conv& c, const void* x, void* y, hipStream
   return gemm_mfma(p, ACT_F16, s);
 }
 
+st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_unet_weights* w,
+                     hipStream_t s, int dev, DevArena* persist, st_unet** out);
+
 // dst [B][C1 + C2][HW] = concat(a [B][C1][HW], b [B][C2][HW]) along channels
 hipError_t concat(void* dst, const void* a, long long C1, const void* b, long long C2, long long HW,
                   int B, hipStream_t s) {
@@ -246,12 +264,50 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
     (void)hipGetLastError();
     return hip_fail(e, "hipGetDevice");
   }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // First build: every allocation from the runtime, sizes counted; then the
+  // handle again, packed into one block of the counted size (DevArena).
+  DevArena count;
+  st_unet* u = nullptr;
+  st_status st = unet_build(cfg, B, H, W, w, s, dev, &count, &u);
+  if (st != ST_OK) return st;
+  free_all(u);
+  delete u;
+  u = nullptr;
   size_t free0 = 0, total = 0;
   (void)hipMemGetInfo(&free0, &total);
+  void* block = nullptr;
+  if (hipMalloc(&block, count.counted) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ST_ERR_OUT_OF_MEMORY, "out of device memory allocating the U-Net's block");
+  }
+  DevArena packed;
+  packed.base = static_cast<char*>(block);
+  packed.cap = count.counted;
+  st = unet_build(cfg, B, H, W, w, s, dev, &packed, &u);
+  if (st != ST_OK) {
+    (void)hipFree(block);
+    return st;
+  }
+  u->allocs.push_back(block);
+  size_t free1 = 0;
+  (void)hipMemGetInfo(&free1, &total);
+  u->bytes = free0 > free1 ? static_cast<unsigned long long>(free0 - free1) : 0ull;
+  *out = u;
+  return ST_OK;
+}
+
+namespace {
+
+// One build of the handle (validated arguments); on failure nothing is kept.
+st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_unet_weights* w,
+                     hipStream_t s, int dev, DevArena* persist, st_unet** out) {
+  const int L = cfg->levels;
+  const int C0 = cfg->channels[0], Td = 4 * C0;
   st_unet* u = new (std::nothrow) st_unet();
   if (!u) return fail(ST_ERR_OUT_OF_MEMORY, "host allocation failed");
   u->cfg = *cfg; u->B = B; u->H = H; u->W = W; u->device = dev;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  u->persist = persist;
   Maker mk{u, s};
   int* overflow = static_cast<int*>(mk.alloc(sizeof(int), "overflow flag"));
   if (overflow) mk.dev(hipMemsetAsync(overflow, 0, sizeof(int), s), "overflow flag");
@@ -273,7 +329,7 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
   u->amid = static_cast<float*>(mk.alloc(sizeof(float) * B * Td, "embedding MLP"));
   u->temb = static_cast<float*>(mk.alloc(sizeof(float) * B * Td, "time embedding"));
   u->temb16 = mk.alloc(2ull * B * Td, "time embedding (bf16)");
-  u->part = static_cast<float2*>(mk.alloc(sizeof(float2) * B * ST_GN_GROUPS * kMaxSplit, "GroupNorm partials"));
+  u->scratch.add(&u->part, sizeof(float2) * B * ST_GN_GROUPS * kMaxSplit);
 
   // parts, in execution order; activation sizes tracked for the buffers
   long long maxmap = static_cast<long long>(B) * 64 * H * W;  // conv_in output at least
@@ -281,7 +337,8 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
   int ri = 0, bi = 0;
   auto add_res = [&](int Ci, int Co, int h, int wd) {
     st_resnet* r = nullptr;
-    if (mk.ok()) mk.part(st_resnet_create(B, Ci, Co, h, wd, Td, 1e-5f, ST_DTYPE_BF16, &w->resnets[ri], s, &r),
+    if (mk.ok()) mk.part(stb_resnet_create(B, Ci, Co, h, wd, Td, 1e-5f, ST_DTYPE_BF16, &w->resnets[ri], s,
+                                           true, persist, &r),
                          "ResnetBlock2D");
     ++ri;
     if (r) u->res.push_back(r);
@@ -289,8 +346,8 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
   };
   auto add_blk = [&](int C, int depth, int h, int wd) {
     st_block* b = nullptr;
-    if (mk.ok()) mk.part(st_block_create(B, C, h, wd, C / 64, cfg->ctx_dim, depth, ST_DTYPE_BF16, &w->blocks[bi],
-                                         s, &b), "Spatial-Transformer block");
+    if (mk.ok()) mk.part(stb_block_create(B, C, h, wd, C / 64, cfg->ctx_dim, depth, ST_DTYPE_BF16,
+                                          &w->blocks[bi], s, true, persist, &b), "Spatial-Transformer block");
     ++bi;
     if (b) u->blk.push_back(b);
   };
@@ -360,7 +417,26 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
       if (cv.ksplit > 1)
         wsf = std::max(wsf, static_cast<long long>(cv.ksplit) * cv.Cout * ((N + 63) / 64 * 64));
     }
-    u->ws = wsf ? static_cast<float*>(mk.alloc(sizeof(float) * wsf, "convolution partial products")) : nullptr;
+    u->ws = nullptr;
+    if (wsf) u->scratch.add(&u->ws, sizeof(float) * wsf);
+  }
+  // operand maps of the convolutions (their padding passes write the halo):
+  // one at a time, so all of them start at the same offset
+  size_t pmax = 0;
+  for (const Conv& cv : u->convs) pmax = std::max(pmax, static_cast<size_t>(cv.prows) * cv.Cp * 2);
+  const size_t pmap_off = u->scratch.reserve(pmax);
+  // the shared arena
+  if (mk.ok()) {
+    size_t arena = u->scratch.bytes;
+    for (st_resnet* r : u->res) arena = std::max(arena, stb_resnet_scratch_bytes(r));
+    for (st_block* b : u->blk) arena = std::max(arena, stb_block_scratch_bytes(b));
+    u->arena = mk.alloc(arena, "shared workspace");
+    if (u->arena) {
+      u->scratch.bind(u->arena);
+      for (Conv& cv : u->convs) cv.P = static_cast<char*>(u->arena) + pmap_off;
+      for (st_resnet* r : u->res) stb_resnet_bind_scratch(r, u->arena);
+      for (st_block* b : u->blk) stb_block_bind_scratch(b, u->arena);
+    }
   }
   if (mk.ok()) mk.dev(hipStreamSynchronize(s), "create: synchronise");
   if (mk.ok() && overflow) {
@@ -378,12 +454,12 @@ ST_API st_status st_unet_create(const st_unet_config* cfg, int B, int H, int W,
     delete u;
     return fail(mk.st, mk.msg);
   }
-  size_t free1 = 0;
-  (void)hipMemGetInfo(&free1, &total);
-  u->bytes = free0 > free1 ? static_cast<unsigned long long>(free0 - free1) : 0ull;
+  u->persist = nullptr;
   *out = u;
   return ST_OK;
 }
+
+}  // namespace
 
 #define UN_TRY(expr, what)                           \
   do {                                               \
