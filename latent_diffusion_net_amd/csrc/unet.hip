@@ -65,7 +65,7 @@ struct st_unet {
   std::vector<void*> skips;       // down-path outputs, in push order
   std::vector<long long> skip_c;  // their channels
   std::vector<int> skip_h, skip_w;
-  void *ta, *tb, *tc, *cat;       // work maps (bf16 NCHW, the largest size)
+  void *ta, *tb, *cat;            // work maps and the concatenation (bf16 NCHW)
   int* range_flag;
   float* ws;                      // split-K partial products of the convolutions
   // The parts run one after another on one stream, so the buffers that each
@@ -331,8 +331,10 @@ st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_un
   u->temb16 = mk.alloc(2ull * B * Td, "time embedding (bf16)");
   u->scratch.add(&u->part, sizeof(float2) * B * ST_GN_GROUPS * kMaxSplit);
 
-  // parts, in execution order; activation sizes tracked for the buffers
-  long long maxmap = static_cast<long long>(B) * 64 * H * W;  // conv_in output at least
+  // parts, in execution order; the largest output held by a work map (a
+  // ResNet's, a transformer block's or an UpSample's) and the largest
+  // concatenation sized for the buffers
+  long long maxwork = 0;
   long long maxcat = 0;
   int ri = 0, bi = 0;
   auto add_res = [&](int Ci, int Co, int h, int wd) {
@@ -342,7 +344,7 @@ st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_un
                          "ResnetBlock2D");
     ++ri;
     if (r) u->res.push_back(r);
-    maxmap = std::max(maxmap, static_cast<long long>(B) * std::max(Ci, Co) * h * wd);
+    maxwork = std::max(maxwork, static_cast<long long>(B) * Co * h * wd);
   };
   auto add_blk = [&](int C, int depth, int h, int wd) {
     st_block* b = nullptr;
@@ -389,7 +391,7 @@ st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_un
       u->convs.push_back(mk.conv(w->up_w[L - 1 - lv], w->up_b ? w->up_b[L - 1 - lv] : nullptr, c, c, h, wd, 1,
                                  1, 0, nullptr, nullptr, overflow, "UpSample"));
       h *= 2; wd *= 2;
-      maxmap = std::max(maxmap, static_cast<long long>(B) * c * h * wd);
+      maxwork = std::max(maxwork, static_cast<long long>(B) * c * h * wd);
     }
   }
   u->convs.push_back(mk.conv(w->conv_out_w, w->conv_out_b, C0, cfg->out_channels, H, W, 1, 0, 1, w->norm_out_w,
@@ -401,10 +403,9 @@ st_status unet_build(const st_unet_config* cfg, int B, int H, int W, const st_un
     u->skip_h.push_back(skh[i]);
     u->skip_w.push_back(skw[i]);
   }
-  u->ta = mk.alloc(2ull * maxmap, "work map");
-  u->tb = mk.alloc(2ull * maxmap, "work map");
-  u->tc = mk.alloc(2ull * maxmap, "work map");
-  u->cat = mk.alloc(2ull * std::max(maxcat, maxmap), "concatenation");
+  u->ta = mk.alloc(2ull * maxwork, "work map");
+  u->tb = mk.alloc(2ull * maxwork, "work map");
+  u->cat = mk.alloc(2ull * maxcat, "concatenation");
   // K slices of the convolutions with few output tiles, one workspace
   {
     int cus = 0;
@@ -527,24 +528,26 @@ ST_API st_status st_unet_forward(st_unet* u, const void* x, const float* t, cons
   h = hout;
   long long ch = c.channels[L - 1];
   // up path: concat(h, skip) -> ResNet (-> transformer), ping-pong over
-  // ta / tb / tc (the concatenation buffer is separate)
+  // ta / tb: the concatenation consumes h, so each part writes the map its
+  // input is not in
+  auto other = [&](const void* m) { return m == u->ta ? u->tb : u->ta; };
   for (int lv = L - 1; lv >= 0; --lv) {
     for (int r = 0; r < c.layers_per_block + 1; ++r) {
       --si;
       const long long hw = static_cast<long long>(u->skip_h[si]) * u->skip_w[si];
       UN_TRY(concat(u->cat, h, ch, u->skips[si], u->skip_c[si], hw, B, s), "skip concatenation");
-      void* r_out = h == u->ta ? u->tb : u->ta;
+      void* r_out = other(h);
       UN_PART(st_resnet_forward(u->res[ri++], u->cat, u->temb16, r_out, s));
       h = r_out;
       ch = c.channels[lv];
       if (c.depths[lv]) {
-        void* b_out = u->tc == h ? u->ta : u->tc;
+        void* b_out = other(h);
         UN_PART(st_block_forward(u->blk[bi++], h, ctx, b_out, s));
         h = b_out;
       }
     }
     if (lv > 0) {
-      void* dst = h == u->ta ? u->tb : u->ta;
+      void* dst = other(h);
       UN_TRY(run_conv(u, u->convs[ci++], h, dst, s), "UpSample");
       h = dst;
     }
