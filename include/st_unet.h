@@ -83,6 +83,11 @@ typedef struct {
  * size and every level's width stays a multiple of 4: H % 2^(levels-1) ==
  * 0 and (W >> (levels-1)) % 4 == 0).  Weights are copied (through the
  * parts' own create calls); `stream` is synchronised before returning.
+ * Memory: the handle's persistent memory (weights, skips, work maps) is one
+ * block of exactly its size (create builds the handle twice: once to count
+ * the sizes, which briefly holds more memory, then into the block), and
+ * the parts' per-forward buffers share one arena of the largest part's
+ * size, since the parts run one after another on `stream`.
  * Errors: ST_ERR_INVALID / ST_ERR_UNSUPPORTED / ST_ERR_OUT_OF_MEMORY /
  * ST_ERR_DEVICE, nothing kept.
  */
@@ -99,7 +104,8 @@ st_status st_unet_create(const st_unet_config *cfg, int B, int H, int W,
 st_status st_unet_forward(st_unet *u, const void *x, const float *t, const void *ctx,
                           const void *add, void *y, void *stream);
 
-/* Device bytes the handle holds (its parts included). */
+/* Device bytes the handle holds (its parts included): the drop of the
+ * device's free memory across the final build in create. */
 st_status st_unet_device_bytes(st_unet *u, unsigned long long *bytes);
 
 /* Range check of every part's fp16 intermediates (st_block_check_range). */
