@@ -491,7 +491,7 @@ st_status stb_block_create(int B, int C, int H, int W, int heads, int D_ctx, int
     cr.dev(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
     // The residual products write [T][C] in 128x128 tiles.  With fewer
     // tiles than CUs (short sequences) each tile has a CU to itself on the
-    // four-stage ring, and K is split into the most slices that keep every
+    // three-stage ring, and K is split into the most slices that keep every
     // slice at least 1024 deep and still give each slice a CU of its own;
     // the slices are summed in order by a second pass.
     {

@@ -6,7 +6,7 @@
 // (WM*FM*32) x (WN*FN*32) outputs, each wavefront FM x FN MFMA blocks of
 // 32x32: 128x128 tiles of four 64x64 wavefronts (two workgroups per CU), or
 // 256x256 tiles of eight 128x64 wavefronts when the product has enough of
-// them.  K advances 64 at a time through two LDS stages (four, with one
+// them.  K advances 64 at a time through two LDS stages (three, with one
 // 128x128 workgroup per CU, when the product has no more tiles than CUs)
 // filled by buffer_load_dwordx4 ... lds (no staging registers), with one
 // barrier per stage; the LDS operand reads of each 16-wide K step are issued while the
@@ -667,18 +667,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   constexpr int DPB = TBN / RPB / NW;    // B blocks per wavefront per stage
   static_assert(DPA * RPB * NW == TBM && DPB * RPB * NW == TBN, "DMA split");
   static_assert(FM % 2 == 0 && FN % 2 == 0, "epilogue works on 64x64 blocks");
-  static_assert(2 * (TBM + TBN) * BKT * 2 >= NW * 16384, "epilogue staging");
-  static_assert(NST == 2 || (NST == 4 && TBM == 128 && NW == 4), "four stages: 128-row tiles");
+  static_assert(NST * (TBM + TBN) * BKT * 2 >= NW * 16384, "epilogue staging");
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   // NST stage buffers per operand, each its own LDS object
-  constexpr int kXA = NST == 4 ? TBM * BKT : 8, kXB = NST == 4 ? TBN * BKT : 8;
+  constexpr int kXA2 = NST == 3 ? TBM * BKT : 8, kXB2 = NST == 3 ? TBN * BKT : 8;
   __shared__ __attribute__((aligned(16))) uint16_t sA0[TBM * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sA1[TBM * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sA2[kXA];
-  __shared__ __attribute__((aligned(16))) uint16_t sA3[kXA];
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[kXA2];
   __shared__ __attribute__((aligned(16))) uint16_t sB0[TBN * BKT];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[TBN * BKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sB2[kXB];
-  __shared__ __attribute__((aligned(16))) uint16_t sB3[kXB];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[kXB2];
   // folded LayerNorm: (rstd, mean * rstd) per row and g per column
   __shared__ __attribute__((aligned(16))) float2 ln_tab[LN ? TBM : 2];
   __shared__ __attribute__((aligned(16))) float ln_gtab[LN ? TBN : 4];
@@ -848,7 +846,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
         }
     }
   }
-  // Four-stage ring (NST == 4): every stage issues one DMA, unconditionally
+  // Three-stage ring (NST == 3): every stage issues one DMA, unconditionally
   // (past the last stage with an empty buffer range, which fetches nothing
   // and zeroes buffers no later stage reads), so that every wait is the same
   // partial count and no branch separates a DMA from the reads after it.
@@ -862,10 +860,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     for (int j2 = 0; j2 < DPB; ++j2) dma16(Bm, bb, sb + (wave * DPB + j2) * 512, boff[j2], sob);
   };
   issue(0, sA0, sB0);
-  if constexpr (NST == 4) {
-    issue_at(1, nk > 1, sA1, sB1);
-    issue_at(2, nk > 2, sA2, sB2);
-  }
+  if constexpr (NST == 3) issue_at(1, nk > 1, sA1, sB1);
   if constexpr (LN) {
     // the sums stay below the DMA issue (the empty statements take the
     // loaded values after it)
@@ -912,14 +907,14 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
     else if (kPF && p.ksplit <= 1) issue_res(wa, wb);
     steps(ca, cb);
   };
-  // Stage k of the four-stage ring waits until its own DMA has landed (the
-  // two issued after it may still be in flight), and after the barrier
-  // refills the buffers that stage k-1 read with stage k+3.
+  // Stage k of the three-stage ring waits until its own DMA has landed (the
+  // one issued after it may still be in flight), and after the barrier
+  // refills the buffers that stage k-1 read with stage k+2.
   constexpr int kPer = DPA + DPB;  // DMA instructions per wavefront per stage
-  auto stage4 = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
-    wait_vmcnt_lds<2 * kPer>();
+  auto stage3 = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
+    wait_vmcnt_lds<kPer>();
     stage_barrier();
-    issue_at(k + 3, k + 3 < nk, wa, wb);
+    issue_at(k + 2, k + 2 < nk, wa, wb);
     steps(ca, cb);
   };
   if constexpr (NST == 2) {
@@ -927,18 +922,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
       stage(k, sA0, sB0, sA1, sB1);
       if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
     }
-  } else {
+  } else if constexpr (NST == 3) {
     int k = 0;
-    for (; k + 4 <= nk; k += 4) {
-      stage4(k, sA0, sB0, sA3, sB3);
-      stage4(k + 1, sA1, sB1, sA0, sB0);
-      stage4(k + 2, sA2, sB2, sA1, sB1);
-      stage4(k + 3, sA3, sB3, sA2, sB2);
+    for (; k + 3 <= nk; k += 3) {
+      stage3(k, sA0, sB0, sA2, sB2);
+      stage3(k + 1, sA1, sB1, sA0, sB0);
+      stage3(k + 2, sA2, sB2, sA1, sB1);
     }
     const int rem = nk - k;
-    if (rem > 0) stage4(k, sA0, sB0, sA3, sB3);
-    if (rem > 1) stage4(k + 1, sA1, sB1, sA0, sB0);
-    if (rem > 2) stage4(k + 2, sA2, sB2, sA1, sB1);
+    if (rem > 0) stage3(k, sA0, sB0, sA2, sB2);
+    if (rem > 1) stage3(k + 1, sA1, sB1, sA0, sB0);
     wait_vmcnt_lds<0>();  // the empty DMAs past the last stage
   }
 
@@ -959,18 +952,19 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   }
   // 16 KB per wavefront: the stage buffers taken in order
   float* stg_area;
-  if constexpr (NST == 4) {
-    // four 16 KB A buffers, one per wavefront
-    uint16_t* a = wave < 2 ? (wave == 0 ? sA0 : sA1) : (wave == 2 ? sA2 : sA3);
-    stg_area = reinterpret_cast<float*>(a);
-  } else {
+  {
+    // wavefront areas in buffer order: sA0, sA1, (sA2,) sB0, sB1, (sB2)
     constexpr int PA = TBM * BKT * 2 / 16384;  // wavefront areas per A buffer
     constexpr int PB = TBN * BKT * 2 / 16384;
+    constexpr int PA2 = NST == 3 ? PA : 0, PB2 = NST == 3 ? PB : 0;
     int w = wave;
     if (w < PA) stg_area = reinterpret_cast<float*>(sA0) + w * 4096;
     else if ((w -= PA) < PA) stg_area = reinterpret_cast<float*>(sA1) + w * 4096;
-    else if ((w -= PA) < PB) stg_area = reinterpret_cast<float*>(sB0) + w * 4096;
-    else stg_area = reinterpret_cast<float*>(sB1) + (w - PB) * 4096;
+    else if ((w -= PA) < PA2) stg_area = reinterpret_cast<float*>(sA2) + w * 4096;
+    else if ((w -= PA2) < PB) stg_area = reinterpret_cast<float*>(sB0) + w * 4096;
+    else if ((w -= PB) < PB) stg_area = reinterpret_cast<float*>(sB1) + w * 4096;
+    else stg_area = reinterpret_cast<float*>(sB2) + (w - PB) * 4096;
+    static_assert(2 * PA + PA2 + 2 * PB + PB2 >= NW, "epilogue areas");
   }
   GemmParams q = p;
   if (p.ksplit > 1) {
@@ -1219,13 +1213,13 @@ static int cu_count() {
   return n;
 }
 
-// Convolutions: 128x128 tiles, two per CU (four-stage ring when there are no
+// Convolutions: 128x128 tiles, two per CU (three-stage ring when there are no
 // more tiles than CUs), or 256x256 tiles when there are many of them.
 static hipError_t launch_conv(const GemmParams& p, hipStream_t s) {
   if (p.ksplit > 1) {
-    // slices one 128x128 workgroup per CU (four-stage ring), then the sum
+    // slices one 128x128 workgroup per CU (three-stage ring), then the sum
     const long long wgs = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128) * p.ksplit;
-    hipError_t e = wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 4>(p, ACT_F16, EPI_CONV, p.ksplit, s)
+    hipError_t e = wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 3>(p, ACT_F16, EPI_CONV, p.ksplit, s)
                                      : launch_pipe<2, 2, 2, 2, 2>(p, ACT_F16, EPI_CONV, p.ksplit, s);
     if (e != hipSuccess) return e;
     const long long n = static_cast<long long>(p.M) * (((p.N + 63) & ~63) >> 2);
@@ -1235,7 +1229,7 @@ static hipError_t launch_conv(const GemmParams& p, hipStream_t s) {
   const long long tiles = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128);
   const long long big = static_cast<long long>((p.M + 255) / 256) * ((p.N + 255) / 256);
   if (big >= kBigTileMin) return launch_pipe<2, 4, 4, 2, 1>(p, ACT_F16, EPI_CONV, 1, s);
-  if (tiles <= cu_count()) return launch_pipe<2, 2, 2, 2, 1, 4>(p, ACT_F16, EPI_CONV, 1, s);
+  if (tiles <= cu_count()) return launch_pipe<2, 2, 2, 2, 1, 3>(p, ACT_F16, EPI_CONV, 1, s);
   return launch_pipe<2, 2, 2, 2, 2>(p, ACT_F16, EPI_CONV, 1, s);
 }
 
@@ -1291,9 +1285,9 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
                   (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))))
       return hipErrorInvalidValue;
     // the slices (the kernel switches to the plain fp32 store; one 128x128
-    // workgroup per CU with four stages when they all fit so), then the sum
+    // workgroup per CU with three stages when they all fit so), then the sum
     const long long slice_wgs = static_cast<long long>((p.M + 127) / 128) * ((p.N + 127) / 128) * split;
-    hipError_t e = slice_wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 4>(p, op, p.epi.kind, split, s)
+    hipError_t e = slice_wgs <= cu_count() ? launch_pipe<2, 2, 2, 2, 1, 3>(p, op, p.epi.kind, split, s)
                                            : launch_pipe<2, 2, 2, 2, 2>(p, op, p.epi.kind, split, s);
     if (e != hipSuccess) return e;
     const long long mn = static_cast<long long>(p.M) * p.N;
@@ -1314,10 +1308,10 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   const long long big_tiles = static_cast<long long>(mtb) * ntb;
   const int cus = cu_count();
   // 128x128 tiles: with no more of them than CUs, one per CU with a
-  // four-stage ring (128 KB of LDS), else two per CU with two stages
+  // three-stage ring (96 KB of LDS), else two per CU with two stages
   auto small_tiles = [&](const GemmParams& q) {
     const long long tiles = static_cast<long long>((q.M + 127) / 128) * ((q.N - q.n_off + 127) / 128);
-    if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 4>(q, op, q.epi.kind, 1, s);
+    if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 3>(q, op, q.epi.kind, 1, s);
     return launch_pipe<2, 2, 2, 2, 2>(q, op, q.epi.kind, 1, s);
   };
   if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN) return small_tiles(p);
