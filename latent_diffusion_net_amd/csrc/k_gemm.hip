@@ -168,9 +168,6 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
       }
     }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (63 & 15) | ((63 >> 4) << 14));  // lgkmcnt(0)
-  bf16x2 one;
-  one[0] = static_cast<__bf16>(1.0f);
-  one[1] = static_cast<__bf16>(1.0f);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int lr = qb * 32 + l32;  // this lane's query within the block
@@ -205,8 +202,10 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
     // P^T step st: block st / 2, entries 8 (st % 2) + 0..7 = keys 16 st + 8 lhi + 0..7;
     // steps past the last key are zero and skipped
     const int nsteps = (ca.nk + 15) >> 4;
+    // row sum of the fp32 exponentials in four independent chains (as the
+    // self-attention kernel does)
     uint4 pb[6];
-    float ps = 0.f;
+    float pa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 6; ++st) {
       if (st >= nsteps) {
@@ -216,14 +215,18 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
       uint32_t w[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
+        const float e0 = __builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj] - mx);
+        const float e1 = __builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj + 1] - mx);
         bf16x2 pk;
-        pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj] - mx));
-        pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[st >> 1][8 * (st & 1) + 2 * jj + 1] - mx));
-        ps = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ps, false);
+        pk[0] = static_cast<__bf16>(e0);
+        pk[1] = static_cast<__bf16>(e1);
+        pa[(2 * jj) & 3] += e0;
+        pa[(2 * jj + 1) & 3] += e1;
         w[jj] = __builtin_bit_cast(uint32_t, pk);
       }
       pb[st] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    const float ps = (pa[0] + pa[1]) + (pa[2] + pa[3]);
     const float ptot = ps + __shfl_xor(ps, 32, 64);
     const float inv = ptot > 0.f ? 1.0f / ptot : 0.f;  // no key: O = 0
     floatx16 o[2];
