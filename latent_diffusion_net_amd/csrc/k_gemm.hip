@@ -37,6 +37,8 @@ namespace {
 
 // Fewest 256x256 tiles for which the large-tile configuration is used.
 constexpr int kBigTileMin = 192;
+// Fewest 256x256 tiles for a product that they cover without padding.
+constexpr int kBigTileExact = 128;
 
 // Output tile of this workgroup (1-D grid of mt * nt workgroups).
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
@@ -1317,7 +1319,12 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
     if (tiles <= cus) return launch_pipe<2, 2, 2, 2, 1, 3>(q, op, q.epi.kind, 1, s);
     return launch_pipe<2, 2, 2, 2, 2>(q, op, q.epi.kind, 1, s);
   };
-  if (big_tiles < kBigTileMin || p.epi.kind == EPI_CROSS_ATTN) return small_tiles(p);
+  // below kBigTileMin, large tiles only where they cover the product with
+  // no padding (FF1 of the U-Net's 1024-token levels at batch 1, 160
+  // tiles: SDXL-Inpaint timestep 17.8 -> 17.0 ms, same box; with padding,
+  // e.g. N = 320, they measured slower)
+  const bool exact = p.M % 256 == 0 && p.N % 256 == 0 && big_tiles >= kBigTileExact;
+  if ((big_tiles < kBigTileMin && !exact) || p.epi.kind == EPI_CROSS_ATTN) return small_tiles(p);
   // When the last round of large tiles would leave more than a quarter of
   // the CUs idle, the columns of whole rounds take large tiles and the rest
   // 128x128 tiles (two per CU) in a second launch.
