@@ -217,6 +217,21 @@ def test_full_config(index):
     gc.collect()
 
 
+def test_unet_level_1024_tokens_batch1():
+    """A transformer block at the shape of the SDXL-Inpaint U-Net's 1024-token
+    levels at batch 1 (32x32, C = 1280, 20 heads): FF1 + GEGLU on 256x256
+    tiles that cover the product exactly (160 of them, fewer than the
+    general threshold), the out-projections and FF2 split over K (80 output
+    tiles), and proj_in on the three-stage ring; every output element
+    against the oracle."""
+    cfg = synth.BlockConfig("b1_c1280_32x32_d1", 1, 1280, 32, 32, 20, 2048, 1, "bf16")
+    inp = synth.make_inputs(cfg, 17)
+    y, _ = run_gpu(cfg, inp)
+    _say("    oracle ...")
+    yo = ob.block_forward(inp["x"], inp["ctx"], inp["params"], cfg.heads)
+    check(cfg, inp, y, yo)
+
+
 def test_deterministic_and_timing():
     import torch
     from latent_diffusion_net_amd import STBlock, array_to_device, params_to_device
