@@ -1000,13 +1000,24 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
 
 // Second pass of split-K: the slices added in order (deterministic), then
 // the epilogue of one element.
+// The reduce kernels issue every slice's loads before the first sum (they
+// are latency-bound launches of a few microseconds): at most kMaxSlices
+// slices (gemm_mfma checks).
+constexpr int kMaxSlices = 8, kMaxConvSlices = 12;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
   const long long mn = static_cast<long long>(p.M) * p.N;
   const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= mn) return;
-  float acc = 0.f;
-  for (int z = 0; z < p.ksplit; ++z) acc += p.ws[z * mn + idx];
+  float v[kMaxSlices];
+#pragma unroll
+  for (int z = 0; z < kMaxSlices; ++z)
+    if (z < p.ksplit) v[z] = p.ws[z * mn + idx];
+  float acc = v[0];
+#pragma unroll
+  for (int z = 1; z < kMaxSlices; ++z)
+    if (z < p.ksplit) acc += v[z];
   const int row = static_cast<int>(idx / p.N);
   epi_store<EPI, bf16_t>(p.epi, row, static_cast<int>(idx - static_cast<long long>(row) * p.N), acc);
 }
@@ -1032,10 +1043,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_conv_kernel(GemmParams p) {
   if (i >= cv.Ho || j >= cv.Wo) return;
   const long long mn = static_cast<long long>(p.M) * ldws;
   const float* w = p.ws + static_cast<long long>(c) * ldws + m0;
-  float4 a = *reinterpret_cast<const float4*>(w);
-  for (int z = 1; z < p.ksplit; ++z) {
-    const float4 v = *reinterpret_cast<const float4*>(w + z * mn);
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  float4 sl[kMaxConvSlices];
+#pragma unroll
+  for (int z = 0; z < kMaxConvSlices; ++z)
+    if (z < p.ksplit) sl[z] = *reinterpret_cast<const float4*>(w + z * mn);
+  float4 a = sl[0];
+#pragma unroll
+  for (int z = 1; z < kMaxConvSlices; ++z) {
+    if (z < p.ksplit) {
+      a.x += sl[z].x; a.y += sl[z].y; a.z += sl[z].z; a.w += sl[z].w;
+    }
   }
   const float add = cv.cadd[static_cast<long long>(b) * p.M + c];
   float y0 = a.x + add, y1 = a.y + add, y2 = a.z + add, y3 = a.w + add;
@@ -1064,26 +1081,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_h16_kernel(GemmParams p) {
   const int c = static_cast<int>(g - row * cpr) * 8;
   const long long mn = static_cast<long long>(p.M) * p.N;
   const float* w = p.ws + row * p.N + c;
-  float v[8];
-  {
-    const float4 a = *reinterpret_cast<const float4*>(w);
-    const float4 b = *reinterpret_cast<const float4*>(w + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  f16_t* h16 = static_cast<f16_t*>(p.epi.out_act) + row * p.epi.ldo + c;
+  float4 sa[kMaxSlices], sb[kMaxSlices];
+#pragma unroll
+  for (int z = 0; z < kMaxSlices; ++z) {
+    if (z < p.ksplit) {
+      sa[z] = *reinterpret_cast<const float4*>(w + z * mn);
+      sb[z] = *reinterpret_cast<const float4*>(w + z * mn + 4);
+    }
   }
-  for (int z = 1; z < p.ksplit; ++z) {
-    const float4 a = *reinterpret_cast<const float4*>(w + z * mn);
-    const float4 b = *reinterpret_cast<const float4*>(w + z * mn + 4);
-    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  uint4 hin = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (RES) hin = *reinterpret_cast<const uint4*>(h16);
+  float v[8] = {sa[0].x, sa[0].y, sa[0].z, sa[0].w, sb[0].x, sb[0].y, sb[0].z, sb[0].w};
+#pragma unroll
+  for (int z = 1; z < kMaxSlices; ++z) {
+    if (z < p.ksplit) {
+      v[0] += sa[z].x; v[1] += sa[z].y; v[2] += sa[z].z; v[3] += sa[z].w;
+      v[4] += sb[z].x; v[5] += sb[z].y; v[6] += sb[z].z; v[7] += sb[z].w;
+    }
   }
   if (p.epi.bias) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] += p.epi.bias[c + k];
   }
-  f16_t* h16 = static_cast<f16_t*>(p.epi.out_act) + row * p.epi.ldo + c;
   if constexpr (RES) {
-    const uint4 hin = *reinterpret_cast<const uint4*>(h16);
     const uint32_t hw[4] = {hin.x, hin.y, hin.z, hin.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1270,7 +1291,8 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   if (p.K % 64) return hipErrorInvalidValue;
   if (p.epi.kind == EPI_CONV) {
     const ConvGemm& cv = p.conv;
-    if (op != ACT_F16 || (p.ksplit > 1 && (!p.ws || p.K % (p.ksplit * 64))) || p.epi.ln_stats ||
+    if (op != ACT_F16 || (p.ksplit > 1 && (!p.ws || p.ksplit > kMaxConvSlices || p.K % (p.ksplit * 64))) ||
+        p.epi.ln_stats ||
         !cv.cadd || !cv.out || cv.spt < 1 ||
         cv.sc_spt < 0 || p.K != (9 * cv.spt + cv.sc_spt) * 64 || cv.Wp % 4 || cv.Wo % 4 ||
         cv.Wo > cv.Wp || cv.Ho > cv.Hq || p.N % (cv.Hq * cv.Wp) || cv.b_bytes <= 0 ||
@@ -1285,7 +1307,7 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   const int split = p.ksplit > 1 ? p.ksplit : 1;
   if (split > 1) {
     const bool h16 = p.epi.kind == EPI_STORE_H16 || p.epi.kind == EPI_RESID_H16;
-    if (!p.ws || p.K % (split * 64) || p.epi.ln_stats ||
+    if (!p.ws || split > kMaxSlices || p.K % (split * 64) || p.epi.ln_stats ||
         (!h16 && (op != ACT_BF16 || p.epi.row_stats ||
                   (p.epi.kind != EPI_HEADS && p.epi.kind != EPI_STORE_F32))))
       return hipErrorInvalidValue;
