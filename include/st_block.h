@@ -234,6 +234,17 @@ st_status st_block_set_timing(st_block *blk, unsigned kind_mask);
 st_status st_block_read_timing(st_block *blk, st_timing *out);
 
 /*
+ * Limits the timing of the per-layer kinds (LayerNorm, Q/K/V, both
+ * attentions, their output projections, the cross Q projection, FF1, FF2)
+ * to the launches of layers 0 .. layers-1 of each forward; 0 (the
+ * default) times every layer, and the other kinds are unaffected.  Each
+ * event pair leaves a bubble of a few microseconds between two kernels,
+ * so timing one layer of a deep block perturbs it less.  ST_ERR_INVALID
+ * for a NULL handle or layers < 0.
+ */
+st_status st_block_set_timing_layers(st_block *blk, int layers);
+
+/*
  * The same recorded launches one by one, in launch order: kinds[i] (an
  * st_kernel_kind) and ms[i] for the first `capacity` of them; *count
  * receives the number recorded.  Clears them, as st_block_read_timing does.

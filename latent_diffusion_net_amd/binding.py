@@ -36,7 +36,7 @@ BLOCK_FIELDS = ("gn_w", "gn_b", "proj_in_w", "proj_in_b", "proj_out_w",
 EXPORTS = ("st_block_create", "st_block_forward", "st_block_forward_masked",
            "st_block_forward_stage",
            "st_block_destroy", "st_block_check_range", "st_last_error",
-           "st_block_set_timing", "st_block_read_timing",
+           "st_block_set_timing", "st_block_set_timing_layers", "st_block_read_timing",
            "st_block_read_timing_launches", "st_measure_mfma_bf16",
            "st_group_norm_workspace_bytes", "st_group_norm", "st_group_norm_noalloc",
            "st_guided_ddpm_step", "st_resnet_create", "st_resnet_forward",
@@ -127,6 +127,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.st_last_error.restype = ctypes.c_char_p
     lib.st_block_set_timing.argtypes = [vp, u]
     lib.st_block_set_timing.restype = i
+    lib.st_block_set_timing_layers.argtypes = [vp, i]
+    lib.st_block_set_timing_layers.restype = i
     lib.st_block_read_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.st_block_read_timing.restype = i
     ll, dbl = ctypes.c_longlong, ctypes.c_double
@@ -258,11 +260,14 @@ class STBlock:
                                                 _stream_handle(stream)))
         return h
 
-    def set_timing(self, kinds=()):
+    def set_timing(self, kinds=(), layers=0):
+        """Time the launches of ``kinds``; the per-layer kinds only in the
+        first ``layers`` layers of each forward (0 = every layer)."""
         mask = 0
         for k in kinds:
             mask |= 1 << (KERNEL_KINDS.index(k) if isinstance(k, str) else int(k))
         _check(self._lib.st_block_set_timing(self._h, mask))
+        _check(self._lib.st_block_set_timing_layers(self._h, int(layers)))
 
     def read_timing(self) -> Dict[str, Dict[str, float]]:
         t = Timing()

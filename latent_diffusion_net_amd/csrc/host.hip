@@ -144,6 +144,9 @@ struct st_block {
   uint32_t* key_bits;
 
   unsigned timing_mask;
+  // per-layer kinds are timed only in layers below timing_layers (0 = all);
+  // timing_layer: the layer being launched (-1 outside the layer loop)
+  int timing_layers, timing_layer;
   std::vector<PendingTiming> pending;
   std::vector<hipEvent_t> spare_events;
 };
@@ -331,6 +334,8 @@ st_status stb_block_create(int B, int C, int H, int W, int heads, int D_ctx, int
   b->bytes_cap = 0;
   if (const char* cap = std::getenv("ST_MAX_DEVICE_BYTES")) b->bytes_cap = std::strtoull(cap, nullptr, 10);
   b->timing_mask = 0;
+  b->timing_layers = 0;
+  b->timing_layer = -1;
   b->range_flag = nullptr;
   b->key_bits = nullptr;
   b->scratch_own = nullptr;
@@ -581,10 +586,12 @@ hipEvent_t take_event(st_block* b) {
   return e;
 }
 
-// Runs `launch` and, if its kind is selected, brackets it with events.
+// Runs `launch` and, if its kind is selected (and, inside the layer loop,
+// its layer is below the timing_layers limit), brackets it with events.
 template <class Fn>
 hipError_t run(st_block* b, int kind, hipStream_t s, Fn&& launch) {
   if (!((b->timing_mask >> kind) & 1u)) return launch();
+  if (b->timing_layers > 0 && b->timing_layer >= b->timing_layers) return launch();
   hipEvent_t e0 = take_event(b), e1 = take_event(b);
   if (!e0 || !e1) {
     if (e0) b->spare_events.push_back(e0);
@@ -703,6 +710,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, const uint8_
 
   for (int l = 0; l < b->depth; ++l) {
     const LayerDev& L = b->L[l];
+    b->timing_layer = l;
     // ---- self-attention sublayer
     if (!bf)
       ST_TRY(run(b, ST_K_LAYERNORM, s, [&] {
@@ -814,6 +822,7 @@ st_status forward_impl(st_block* b, const void* x, const void* ctx, const uint8_
     ++stage;
     if (dump()) break;
   }
+  b->timing_layer = -1;
   if (stop_stage >= 0) {
     if (stage != stop_stage) return fail(ST_ERR_INVALID, "stage out of range");
     ST_TRY(dump_h(), "stage copy");
@@ -941,6 +950,14 @@ ST_API st_status st_block_set_timing(st_block* b, unsigned kind_mask) {
   g_err.clear();
   if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
   b->timing_mask = kind_mask & ((1u << ST_K_COUNT) - 1u);
+  return ST_OK;
+}
+
+ST_API st_status st_block_set_timing_layers(st_block* b, int layers) {
+  g_err.clear();
+  if (!b) return fail(ST_ERR_INVALID, "handle is NULL");
+  if (layers < 0) return fail(ST_ERR_INVALID, "layers must be >= 0");
+  b->timing_layers = layers;
   return ST_OK;
 }
 

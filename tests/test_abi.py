@@ -196,6 +196,7 @@ def test_null_handle_new_entry_points():
     d = ctypes.c_double()
     assert lib.st_measure_mfma_bf16(0, None, ctypes.byref(d), ctypes.byref(d)) \
         == binding.ST_ERR_INVALID
+    assert lib.st_block_set_timing_layers(None, 1) == binding.ST_ERR_INVALID
 
 
 def test_ops_validate_before_any_device_call():

@@ -252,6 +252,16 @@ def test_deterministic_and_timing():
     assert t["self_attn"]["ms"] > 0
     assert "qkv" not in t
     assert blk.read_timing() == {}
+    # the per-layer kinds timed in the first layer only; the block-level
+    # kinds (proj_out) in every forward; outputs unchanged
+    blk.set_timing(["self_attn", "ff2", "proj_out"], layers=1)
+    y3 = blk.forward(x, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    t = blk.read_timing()
+    assert t["self_attn"]["launches"] == 1 and t["ff2"]["launches"] == 1
+    assert t["proj_out"]["launches"] == 1
+    blk.set_timing([])
     blk.close()
 
 
