@@ -132,8 +132,10 @@ __device__ __forceinline__ bool f16_pair_nonfinite(uint32_t d) {
   return ((d & 0x7c00u) == 0x7c00u) | ((d & 0x7c000000u) == 0x7c000000u);
 }
 __device__ __forceinline__ bool f16x8_nonfinite(const uint4& w) {
-  return f16_pair_nonfinite(w.x) | f16_pair_nonfinite(w.y) | f16_pair_nonfinite(w.z) |
-         f16_pair_nonfinite(w.w);
+  // the four tests OR-ed without branches
+  const int any = static_cast<int>(f16_pair_nonfinite(w.x)) | static_cast<int>(f16_pair_nonfinite(w.y)) |
+                  static_cast<int>(f16_pair_nonfinite(w.z)) | static_cast<int>(f16_pair_nonfinite(w.w));
+  return any != 0;
 }
 
 // s_waitcnt that waits for vmcnt <= n and for every LDS access of this

@@ -190,7 +190,7 @@ struct Creator {
   st_block* b;
   hipStream_t s;
   st_status st = ST_OK;
-  std::string msg;
+  std::string msg{};
 
   bool ok() const { return st == ST_OK; }
   void oom(const char* what) {

@@ -411,7 +411,6 @@ __global__ __launch_bounds__(64 * NW, QB == 1 && NW >= 4 ? 3 : 2) void attn_bf16
   // way at 1024 tokens), and so does the 77-key kernel (two key tiles; the
   // read-ahead would spill its key-mask words inside the loop).
   constexpr bool kReadAhead = NW >= 4 && KIND == 0;
-  const int tlast = kt1 - 1;
   auto iter = [&](int t, const uint16_t* kn, const uint16_t* vc, uint16_t* kw, uint16_t* vw) {
     if (t + 3 < ntiles) issue_k(kt0 + t + 3, kw);
     if (t + 2 < ntiles) issue_v(kt0 + t + 2, vw);

@@ -443,7 +443,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
           pack2h((v.x + bv[0]) * gelu_as(g.x + bg[0]), (v.y + bv[1]) * gelu_as(g.y + bg[1])),
           pack2h((v.z + bv[2]) * gelu_as(g.z + bg[2]), (v.w + bv[3]) * gelu_as(g.w + bg[3])));
       *reinterpret_cast<uint2*>(out + static_cast<long long>(row) * F + fc0 + lc) = pk;
-      bad |= f16_pair_nonfinite(pk.x) | f16_pair_nonfinite(pk.y);
+      bad |= (static_cast<int>(f16_pair_nonfinite(pk.x)) | static_cast<int>(f16_pair_nonfinite(pk.y))) != 0;
     }
     if (bad && p.epi.range_flag) *p.epi.range_flag = 1;
   } else if constexpr (EPI == EPI_HEADS) {

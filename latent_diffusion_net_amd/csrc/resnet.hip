@@ -80,7 +80,7 @@ struct Maker {
   st_resnet* r;
   hipStream_t s;
   st_status st = ST_OK;
-  std::string msg;
+  std::string msg{};
   bool ok() const { return st == ST_OK; }
   void dev(hipError_t e, const char* what) {
     if (ok() && e != hipSuccess) { st = ST_ERR_DEVICE; msg = std::string(what) + ": " + hipGetErrorString(e); }
