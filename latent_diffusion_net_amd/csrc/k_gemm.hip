@@ -103,6 +103,17 @@ __device__ __forceinline__ int kperm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Staging of Q in the cross-attention epilogue: the 16-byte chunk k of row r
+// is stored at chunk k ^ g(r), g(r) = r mod 16 with bits 2 and 3 swapped.
+// The read-back gives each lane its own row (16 consecutive rows per
+// 16-lane read phase, one chunk each: 16 distinct chunks, all 64 banks);
+// the accumulator stores write rows r and r + 4 (bit 2 of r differs, so
+// bit 3 of g differs) into disjoint halves of the banks.
+__device__ __forceinline__ int qstg(int row, int col) {
+  const int g = (row & 3) | ((row & 8) >> 1) | ((row & 4) << 1);
+  return row * 64 + ((((col >> 2) ^ g) << 2) | (col & 3));
+}
+
 // EPI_CROSS_ATTN for one 64x64 block (64 queries of one sample, one head):
 // Q = (acc [LayerNorm-corrected] + bias) * scale is staged in LDS and read
 // back as bf16 B operands; for each 32-query half, S^T = K Q^T over three
@@ -165,7 +176,7 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
         for (int j = 0; j < 2; ++j) {
           float v = acc[i][j][r];
           if constexpr (LN) v = fmaf(v, k[jj].x, -k[jj].y * gj[j]);
-          stage[stg(lr0 + jj, j * 32 + l32)] = (v + bj[j]) * ca.scale;
+          stage[qstg(lr0 + jj, j * 32 + l32)] = (v + bj[j]) * ca.scale;
         }
       }
     }
@@ -176,8 +187,8 @@ __device__ __forceinline__ void cross_attn_block(const GemmParams& p, const floa
     uint4 qop[4];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const float4 a = *reinterpret_cast<const float4*>(&stage[stg(lr, 16 * s4 + 8 * lhi)]);
-      const float4 c = *reinterpret_cast<const float4*>(&stage[stg(lr, 16 * s4 + 8 * lhi + 4)]);
+      const float4 a = *reinterpret_cast<const float4*>(&stage[qstg(lr, 16 * s4 + 8 * lhi)]);
+      const float4 c = *reinterpret_cast<const float4*>(&stage[qstg(lr, 16 * s4 + 8 * lhi + 4)]);
       qop[s4] = make_uint4(pack2bf(a.x, a.y), pack2bf(a.z, a.w), pack2bf(c.x, c.y), pack2bf(c.z, c.w));
     }
     floatx16 sc[3];
