@@ -39,6 +39,8 @@ namespace {
 constexpr int kBigTileMin = 192;
 // Fewest 256x256 tiles for a product that they cover without padding.
 constexpr int kBigTileExact = 128;
+// Shallowest product (K) that takes 256x256 tiles.
+constexpr int kBigTileMinK = 640;
 
 // Output tile of this workgroup (1-D grid of mt * nt workgroups).
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
@@ -1357,7 +1359,13 @@ hipError_t gemm_mfma(const GemmParams& p, int op, hipStream_t s) {
   // tiles: SDXL-Inpaint timestep 17.8 -> 17.0 ms, same box; with padding,
   // e.g. N = 320, they measured slower)
   const bool exact = p.M % 256 == 0 && p.N % 256 == 0 && big_tiles >= kBigTileExact;
-  if ((big_tiles < kBigTileMin && !exact) || p.epi.kind == EPI_CROSS_ATTN) return small_tiles(p);
+  // Products shallower than 640 (five 64-deep stages at C = 320) keep
+  // 128x128 tiles two per CU: the two workgroups of a CU overlap each
+  // other's prologue and epilogue, which such short K loops cannot hide
+  // (SD2.1 Down0: Q/K/V 33-36 -> 27-32 us, forward -1%; SD2.1-base
+  // timestep -0.5-0.8%, same box).
+  if ((big_tiles < kBigTileMin && !exact) || p.epi.kind == EPI_CROSS_ATTN || p.K < kBigTileMinK)
+    return small_tiles(p);
   // When the last round of large tiles would leave more than a quarter of
   // the CUs idle, the columns of whole rounds take large tiles and the rest
   // 128x128 tiles (two per CU) in a second launch.
