@@ -59,13 +59,25 @@ __global__ __launch_bounds__(kGnThreads) void gn_partial_kernel(
     float d = to_f32<T>(x[i]) - shift;
     s1 += d; s2 += d * d;
   }
-  for (long long i = vlo + 8LL * threadIdx.x; i < vhi; i += 8LL * kGnThreads) {
-    float v[8];
+  // two vectors per thread and step, both loads issued before either is
+  // summed (the same order of additions as one vector per step)
+  constexpr long long kStep = 8LL * kGnThreads;
+  for (long long i = vlo + 8LL * threadIdx.x; i < vhi; i += 2 * kStep) {
+    float v[8], w[8];
+    const bool two = i + kStep < vhi;
     load8<T>(x + i, v);
+    if (two) load8<T>(x + i + kStep, w);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float d = v[j] - shift;
       s1 += d; s2 += d * d;
+    }
+    if (two) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float d = w[j] - shift;
+        s1 += d; s2 += d * d;
+      }
     }
   }
   for (long long i = vhi + threadIdx.x; i < hi; i += kGnThreads) {
@@ -144,17 +156,34 @@ __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
   const int b = blockIdx.z;
   const int cg = C / kGroups;
   const int tid = threadIdx.x;
+  // The tile's loads go out first: they do not depend on the coefficients,
+  // whose chain of dependent loads and fp64 sums then runs in their shadow.
+  const bool vec_n = (N & 7) == 0;
+  float v[2][8];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = pass * 32 + (tid >> 3);
+    const int n = n0 + 8 * (tid & 7);
+    const TI* src = x + (static_cast<long long>(b) * C + c0 + cl) * N + n;
+    if (vec_n && n + 7 < N) {
+      load8<TI>(src, v[pass]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[pass][j] = n + j < N ? to_f32<TI>(src[j]) : 0.f;
+    }
+  }
   if (tid < 64) {
     const int c = c0 + tid;
     const int g = b * kGroups + c / cg;
+    const double shift = to_f32<TI>(x[static_cast<long long>(g) * cg * N]);
     double s1 = 0.0, s2 = 0.0;
+#pragma unroll 4
     for (int i = 0; i < split; ++i) {
       const float2 pr = partial[g * split + i];
       s1 += pr.x;
       s2 += pr.y;
     }
     const double n = static_cast<double>(cg) * N;
-    const double shift = to_f32<TI>(x[static_cast<long long>(g) * cg * N]);
     const double dm = s1 / n;
     double var = s2 / n - dm * dm;
     if (var < 0.0) var = 0.0;
@@ -163,23 +192,13 @@ __global__ __launch_bounds__(256) void gn_apply_tokens_kernel(
     coef[tid] = make_float2(scale, beta[c] - static_cast<float>(shift + dm) * scale);
   }
   __syncthreads();
-  const bool vec_n = (N & 7) == 0;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int cl = pass * 32 + (tid >> 3);
     const int nl = 8 * (tid & 7);
-    const int n = n0 + nl;
     const float2 k = coef[cl];
-    const TI* src = x + (static_cast<long long>(b) * C + c0 + cl) * N + n;
-    float v[8];
-    if (vec_n && n + 7 < N) {
-      load8<TI>(src, v);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = n + j < N ? to_f32<TI>(src[j]) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[cl][nl + j] = v[j] * k.x + k.y;
+    for (int j = 0; j < 8; ++j) tile[cl][nl + j] = v[pass][j] * k.x + k.y;
   }
   __syncthreads();
   bool bad = false;
