@@ -1,13 +1,16 @@
 """Self-attention sublayer checks with a non-flat softmax (shared by the GPU
 parity tests and the CPU mutation checks of their bounds).
 
-The shapes reach every variant of the bf16 self-attention that the headline
-workload runs: the 128-query kernel at the full SDXL Down1 shape (B=2,
+The shapes reach every variant of the bf16 self-attention that the
+workloads run: the 128-query kernel at the full SDXL Down1 shape (B=2,
 C=640, 64x64 tokens, 10 heads: 640 query tiles on 256 CUs, so whole tiles
 plus tiles split over their keys into pieces and merged), the same kernel
 with ragged queries and keys (63x63 = 3969 tokens: the last query tile has
-one query, the last key tile one key), and the key-split plans forced at a
-small size by planning for fewer CUs (``cus``).
+one query, the last key tile one key), the key-split plans forced at a
+small size by planning for fewer CUs (``cus``), and the overlapped kernel
+that takes plans without a key split (the SD2.1 Down0 shape, 9216 tokens,
+and the ragged shape planned so that nothing is split).  ``pins=False``
+leaves a shape out of the CPU mutation checks (the oracle's cost there).
 
 The query and key weights are drawn with std sqrt(3 / C), so the logits
 have a standard deviation of about 3 (a softmax far from flat: at 4096 keys
@@ -45,6 +48,12 @@ SHAPES = [
     dict(name="split2", B=1, C=64, H=64, W=64, D_ctx=64, cus=12),
     dict(name="split3_ragged", B=1, C=64, H=63, W=63, D_ctx=64, cus=31),
     dict(name="split2_all", B=1, C=64, H=64, W=64, D_ctx=64, cus=64),
+    # whole query tiles only (no key split): the overlapped kernel, at the
+    # SD2.1 Down0 shape (720 tiles on 512 persistent workgroups, so some take
+    # two) and with ragged queries and keys (planned for 320 CUs: 640 tiles,
+    # no remainder to split)
+    dict(name="sd21_down0_b2_c320_96x96", B=2, C=320, H=96, W=96, D_ctx=1024, cus=None, pins=False),
+    dict(name="b2_c640_63x63_ragged_whole", B=2, C=640, H=63, W=63, D_ctx=128, cus=320),
 ]
 
 

@@ -51,7 +51,7 @@ MUTATIONS = {"flat": _flat, "half": _half, "unweighted_merge": _unweighted_merge
 
 # the forced split plans and the ragged C=640 shape every time; the full
 # SDXL Down1 shape too (about 90 GFLOP of fp64 attention per evaluation)
-SPECS = [s for s in sa.SHAPES]
+SPECS = [s for s in sa.SHAPES if s.get("pins", True)]
 
 
 @pytest.mark.parametrize("spec", SPECS, ids=lambda s: s["name"])
