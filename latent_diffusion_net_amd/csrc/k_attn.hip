@@ -691,7 +691,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_sa_kernel(AttnParams p) {
     // all four at the top of the iteration); past the last tile it reloads
     // that tile, so the DMA is unconditional and the offsets stay in range
     // phase 1 (nxt still holds the exponentials of tile t-1)
-    float mt = cur[0][0];
+    // (two independent max chains: one wavefront per SIMD, as in the last
+    // round of a persistent grid, cannot hide a dependent pair per chunk)
+    float mt0 = cur[0][0], mt1 = cur[0][1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if constexpr (!FIRST) {
@@ -699,12 +701,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_sa_kernel(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ls[j] += nxt[i >> 2][4 * (i & 3) + j];
         const int kb = i >> 2, r0 = 4 * (i & 3);
-        mt = max3f(mt, cur[kb][r0], cur[kb][r0 + 1]);
-        mt = max3f(mt, cur[kb][r0 + 2], cur[kb][r0 + 3]);
+        mt0 = max3f(mt0, cur[kb][r0], cur[kb][r0 + 1]);
+        mt1 = max3f(mt1, cur[kb][r0 + 2], cur[kb][r0 + 3]);
       }
       ka[i] = lds_operand(kn, i & 1, i >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    float mt = fmaxf(mt0, mt1);
     if constexpr (!FIRST) {
       if (__any(mt > kLazyExp)) {  // rare
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
@@ -728,6 +731,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_sa_kernel(AttnParams p) {
     // K steps), exponentials [32i/10, 32(i+1)/10) of S_t with the packs of
     // completed pairs, and the read of va[i].
     uint32_t pw[16];
+    auto pack_pairs = [&](int k0, int k1) {
+#pragma unroll
+      for (int k = k0; k < k1; ++k)
+        if (k & 1) {
+          pw[k >> 1] = pack2bf(cur[(k - 1) >> 4][(k - 1) & 15], cur[k >> 4][k & 15]);
+          asm volatile("" : "+v"(pw[k >> 1]));
+        }
+    };
     const int kdma = min(kt0 + t + 3, kt1 - 1), vdma = min(kt0 + t + 2, kt1 - 1);
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
@@ -743,20 +754,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_sa_kernel(AttnParams p) {
 #pragma unroll
       for (int k = (32 * i) / 10; k < (32 * (i + 1)) / 10; ++k) {
         cur[k >> 4][k & 15] = __builtin_amdgcn_exp2f(cur[k >> 4][k & 15]);
-        // pin the exponential and the pack to this chunk (otherwise they
-        // sink to their first use in the next iteration)
+        // pin the exponential to this chunk (otherwise it sinks to its
+        // first use in the next iteration)
         asm volatile("" : "+v"(cur[k >> 4][k & 15]));
-        if (k & 1) {
-          pw[k >> 1] = pack2bf(cur[(k - 1) >> 4][(k - 1) & 15], cur[k >> 4][k & 15]);
-          asm volatile("" : "+v"(pw[k >> 1]));
-        }
       }
+      // packs of the pairs completed in the previous chunk, one chunk after
+      // their exponentials (a pack right behind its exp2 waits for it)
+      if (i > 0) pack_pairs((32 * (i - 1)) / 10, (32 * i) / 10);
       if (i < 8) va[i] = lds_operand(vc, i & 1, i >> 1);
       if (i >= 1 && i <= BPW) tile_dma(K, kv_bytes, kw + (wave * BPW + i - 1) * 512, koff[i - 1], kdma * KT * 128);
       if (i > BPW && i <= 2 * BPW)
         tile_dma(VT, kv_bytes, vw + (wave * BPW + i - 1 - BPW) * 512, voff[i - 1 - BPW], vdma * KT * 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    pack_pairs(28, 32);
 #pragma unroll
     for (int st = 0; st < 4; ++st) pb[st] = make_uint4(pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]);
     if (kt0 + t + 1 == ragged_last) mask_tile(kt0 + t + 1, nxt);
