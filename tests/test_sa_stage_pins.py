@@ -10,7 +10,14 @@ are what a wrong K tile, rescale or merge in the kernel would produce:
   * half     -- the keys of the second half dropped (a missing key piece);
   * unweighted merge -- two key pieces each normalised on its own and
                 averaged, without their maxima and row sums;
-  * no scale -- softmax(Q K^T) without the 1/sqrt(64).
+  * no scale -- softmax(Q K^T) without the 1/sqrt(64);
+  * no rescale -- keys taken in tiles of 64 against a lazy reference max
+                (raised when a tile's max exceeds it by more than 8 in base
+                2, as both kernels do), with the row sums rescaled but the
+                accumulated output not.
+A further check counts, on the oracle's own scores, how many queries take
+at least one such lazy rescale, so that the GPU tests are known to reach
+that path.
 """
 import numpy as np
 import pytest
@@ -46,8 +53,54 @@ def _no_scale(q, k, v, heads, **kw):
     return _attention(8.0 * np.asarray(q, np.float64), k, v, heads)
 
 
+LAZY_BOUND = 8.0  # base-2 excess over the reference max that forces a rescale
+
+
+def _lazy_events(s2):
+    """Rescale events per row of base-2 scores s2 [rows, keys] under the
+    lazy rule (tile 0 sets the reference max exactly)."""
+    nt = (s2.shape[1] + 63) // 64
+    m = s2[:, :64].max(axis=1)
+    ev = np.zeros(s2.shape[0], np.int64)
+    for t in range(1, nt):
+        mt = s2[:, 64 * t:64 * t + 64].max(axis=1)
+        big = mt > m + LAZY_BOUND
+        ev += big
+        m = np.where(big, mt, m)
+    return ev
+
+
+def _no_rescale(q, k, v, heads, **kw):
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Nq, C = q.shape
+    Nk = k.shape[1]
+    out = np.empty((B, Nq, C))
+    for b in range(B):
+        for hd in range(heads):
+            sl = slice(64 * hd, 64 * hd + 64)
+            s2 = (q[b, :, sl] @ k[b, :, sl].T) / 8.0 * np.log2(np.e)
+            m = s2[:, :64].max(axis=1)
+            e = np.exp2(s2[:, :64] - m[:, None])
+            o = e @ v[b, :64, sl]
+            l = e.sum(axis=1)
+            for t in range(1, (Nk + 63) // 64):
+                st = s2[:, 64 * t:64 * t + 64]
+                mt = st.max(axis=1)
+                big = mt > m + LAZY_BOUND
+                m_new = np.where(big, mt, m)
+                l = l * np.exp2(m - m_new)  # the output is (wrongly) not rescaled
+                m = m_new
+                e = np.exp2(st - m[:, None])
+                o = o + e @ v[b, 64 * t:64 * t + 64, sl]
+                l = l + e.sum(axis=1)
+            out[b, :, sl] = o / l[:, None]
+    return out
+
+
 MUTATIONS = {"flat": _flat, "half": _half, "unweighted_merge": _unweighted_merge,
-             "no_scale": _no_scale}
+             "no_scale": _no_scale, "no_rescale": _no_rescale}
 
 # the forced split plans and the ragged C=640 shape every time; the full
 # SDXL Down1 shape too (about 90 GFLOP of fp64 attention per evaluation)
@@ -75,3 +128,23 @@ def test_mutations_exceed_update_bounds(spec):
         rel, mx = sa.update_errors(hm - h0, d_ref)
         print(f"{spec['name']} {name}: rel_l2={rel:.3e} max_abs/max={mx:.3e}")
         assert rel > MARGIN * sa.UPDATE_REL_L2, (name, rel)
+
+
+@pytest.mark.parametrize("spec", [s for s in SPECS if s["cus"] is None], ids=lambda s: s["name"])
+def test_sharp_inputs_reach_the_lazy_rescale(spec):
+    """At the full-size sharp shapes a good share of the queries see a key
+    tile whose maximum exceeds the running reference by more than 8 (base
+    2), so the kernels' rescale path runs in the GPU tests (head 0, every
+    8th query of sample 0)."""
+    cfg, inp = sa.inputs(spec)
+    p = inp["params"]
+    lw = p["layers"][0]
+    z = ob.group_norm(inp["x"][:1], p["gn_w"], p["gn_b"])
+    h0 = ob.linear(ob.to_tokens(z), p["proj_in_w"], p.get("proj_in_b"))
+    u = ob.layer_norm(h0, lw["ln1_w"], lw["ln1_b"])
+    q = ob.linear(u[:, ::8], lw["q1_w"][:64], None if lw.get("q1_b") is None else lw["q1_b"][:64])
+    k = ob.linear(u, lw["k1_w"][:64], None if lw.get("k1_b") is None else lw["k1_b"][:64])
+    ev = _lazy_events((q[0] @ k[0].T) / 8.0 * np.log2(np.e))
+    share = float((ev > 0).mean())
+    print(f"{spec['name']}: {share:.2f} of the queries take a lazy rescale")
+    assert share >= 0.1, share
