@@ -929,16 +929,81 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_pipe_kernel(GemmParam
   // one issued after it may still be in flight), and after the barrier
   // refills the buffers that stage k-1 read with stage k+2.
   constexpr int kPer = DPA + DPB;  // DMA instructions per wavefront per stage
+  // The three-stage ring issues its DMA spread over the stage's MFMA
+  // groups (a quarter after each) instead of all before them.
+  // (bk: the B offset of stage k, from next_boff, called once per stage)
+  auto dma_one = [&](int j, int k, int bk, bool valid, uint16_t* sa, uint16_t* sb) {
+    if (j < DPA) {
+      const int ab = valid ? abytes : 0, so = valid ? k * BKT * 2 : 0;
+      dma16(A, ab, sa + (wave * DPA + j) * 512, aoff[j], so);
+    } else {
+      const int bb = valid ? bbytes : 0, sob = valid ? bk : 0;
+      dma16(Bm, bb, sb + (wave * DPB + j - DPA) * 512, boff[j - DPA], sob);
+    }
+  };
+  auto steps_dma = [&](const uint16_t* ca, const uint16_t* cb, int k2, bool valid, uint16_t* wa, uint16_t* wb) {
+    constexpr int Q = (DPA + DPB) / 4;
+    static_assert(4 * Q == DPA + DPB, "DMA quarters");
+    const int bk = next_boff(k2);
+    rd(ca, cb, 0, xa, xb);
+    rd(ca, cb, 1, ya, yb);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) dma_one(j, k2, bk, valid, wa, wb);
+    mm(xa, xb);
+    rd(ca, cb, 2, xa, xb);
+#pragma unroll
+    for (int j = Q; j < 2 * Q; ++j) dma_one(j, k2, bk, valid, wa, wb);
+    mm(ya, yb);
+    rd(ca, cb, 3, ya, yb);
+#pragma unroll
+    for (int j = 2 * Q; j < 3 * Q; ++j) dma_one(j, k2, bk, valid, wa, wb);
+    mm(xa, xb);
+#pragma unroll
+    for (int j = 3 * Q; j < 4 * Q; ++j) dma_one(j, k2, bk, valid, wa, wb);
+    mm(ya, yb);
+    constexpr int R = FM + FN, F = FM * FN;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, Q, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, Q, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, Q, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, Q, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, F, 0);
+  };
   auto stage3 = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
     wait_vmcnt_lds<kPer>();
     stage_barrier();
-    issue_at(k + 2, k + 2 < nk, wa, wb);
-    steps(ca, cb);
+    steps_dma(ca, cb, k + 2, k + 2 < nk, wa, wb);
   };
-  if constexpr (NST == 2) {
+  if constexpr (NST == 2 && (WM != 2 || WN != 2)) {
+    // 256x256 tiles: the next stage's DMA at the top of each stage (spread
+    // over the MFMA groups, the stores-only epilogues of these tiles spill)
     for (int k = 0; k < nk; k += 2) {
       stage(k, sA0, sB0, sA1, sB1);
       if (k + 1 < nk) stage(k + 1, sA1, sB1, sA0, sB0);
+    }
+  } else if constexpr (NST == 2) {
+    // every stage but the last issues the next one's DMA spread over its
+    // MFMA groups; the last issues the residual prefetch (or nothing)
+    auto stage_mid = [&](int k, const uint16_t* ca, const uint16_t* cb, uint16_t* wa, uint16_t* wb) {
+      wait_vmcnt_lds<0>();
+      stage_barrier();
+      steps_dma(ca, cb, k + 1, true, wa, wb);
+    };
+    int k = 0;
+    for (; k + 2 < nk; k += 2) {
+      stage_mid(k, sA0, sB0, sA1, sB1);
+      stage_mid(k + 1, sA1, sB1, sA0, sB0);
+    }
+    if (nk - k == 2) {
+      stage_mid(k, sA0, sB0, sA1, sB1);
+      stage(k + 1, sA1, sB1, sA0, sB0);
+    } else {
+      stage(k, sA0, sB0, sA1, sB1);
     }
   } else if constexpr (NST == 3) {
     int k = 0;
