@@ -124,7 +124,8 @@ typedef struct {
  * memory the handle may allocate (beyond it create fails with
  * ST_ERR_OUT_OF_MEMORY); ST_ATTN_CUS overrides the CU count that the bf16
  * self-attention's load-balance plan assumes (it changes only how the work
- * is split, not the result beyond rounding order; for tests).
+ * is split over keys, and with it which of the two self-attention kernels
+ * runs -- not the result beyond rounding order; for tests).
  */
 st_status st_block_create(int B, int C, int H, int W, int heads, int D_ctx,
                           int depth, st_dtype dtype, const st_block_weights *w,
