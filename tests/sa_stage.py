@@ -54,6 +54,13 @@ SHAPES = [
     # no remainder to split)
     dict(name="sd21_down0_b2_c320_96x96", B=2, C=320, H=96, W=96, D_ctx=1024, cus=None, pins=False),
     dict(name="b2_c640_63x63_ragged_whole", B=2, C=640, H=63, W=63, D_ctx=128, cus=320),
+    # the overlapped kernel on few key tiles (many samples and heads, so
+    # that the plan still has at least two query tiles per CU): four key
+    # tiles (its loop's tail iterations only) and a single one; left out of
+    # the CPU mutation checks, which need several key tiles to mean anything
+    # (a single tile takes no lazy rescale)
+    dict(name="b32_c1024_16x16_four_key_tiles", B=32, C=1024, H=16, W=16, D_ctx=64, cus=None, pins=False),
+    dict(name="b32_c1024_8x8_one_key_tile", B=32, C=1024, H=8, W=8, D_ctx=64, cus=None, pins=False),
 ]
 
 
